@@ -1,0 +1,226 @@
+"""Benchmark of the SmoothQuant W8A8 linear layer on one MI355X.
+
+One step = the whole path over one batch of the workload, for every site of it:
+calibration absmax -> smoothing fold (s, folded norm, INT8 weights) -> fused
+norm + per-token INT8 quantisation -> INT8 GEMM with dequant epilogue.
+Default workload: the MT-NLG-530B-width layer (hidden 20480: LayerNorm -> fc1
+20480 -> 81920 and fc2 81920 -> 20480 at 8192 tokens, fp16), the largest
+single-GPU prefill configuration.
+
+Prints one JSON line. `value` is the step's GEMM work (2*M*N*K summed over the
+sites) divided by the step time, in TOPS; `roofline` reports the GEMM kernel
+against the INT8 dense MFMA peak from HIP events around each launch; `kernels`
+gives every stage's average duration and its achieved rate; `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+EPS = 1e-5
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=5)
+    p.add_argument("--m", type=int, default=None, help="token count (workloads with several)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run one plain device copy of this size (counter calibration runs)")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the stream the library launches on, one pair per launch."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def run(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.ev.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        pairs = self.ev.get(name, [])
+        return sum(s.elapsed_time(e) for s, e in pairs) / max(1, len(pairs))
+
+    def reset(self):
+        self.ev = {}
+
+
+def build_sites(torch, sq, wl, m):
+    from synth import site_inputs
+    sites = []
+    out_dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.out_dtype]
+    for si, site in enumerate(wl.sites):
+        inp = site_inputs(wl.id, si, m=m, device="cuda")
+        k, n = site.k, site.n
+        d = dict(inp, norm=site.norm, k=k, n=n, m=m,
+                 absmax=torch.zeros(k, dtype=torch.float32, device="cuda"),
+                 fold=None,
+                 xq=torch.empty(m, k, dtype=torch.int8, device="cuda"),
+                 xs=torch.empty(m, dtype=torch.float32, device="cuda"),
+                 y=torch.empty(m, n, dtype=out_dt, device="cuda"))
+        d["fold"] = {"s": torch.empty(k, dtype=torch.float32, device="cuda"),
+                     "gamma_f": torch.empty(k, dtype=torch.float32, device="cuda"),
+                     "wq": torch.empty(n, k, dtype=torch.int8, device="cuda"),
+                     "w_scale": torch.empty(n, dtype=torch.float32, device="cuda")}
+        if inp["beta"] is not None:
+            d["fold"]["beta_f"] = torch.empty(k, dtype=torch.float32, device="cuda")
+        sites.append(d)
+    torch.cuda.synchronize()
+    return sites
+
+
+def step(sq, wl, sites, timer):
+    for i, d in enumerate(sites):
+        d["absmax"].zero_()
+        timer.run(f"calibrate{i}", lambda: sq.smoothquant_calibrate(d["x_cal"], d["norm"], d["gamma"], d["beta"],
+                                                                    EPS, absmax=d["absmax"]))
+        timer.run(f"fold{i}", lambda: sq.smoothquant_fold(d["absmax"], d["w"], wl.alpha, EPS, d["norm"], d["gamma"],
+                                                          d["beta"], out=d["fold"]))
+        f = d["fold"]
+        timer.run(f"norm_quant{i}", lambda: sq.sq_norm_quant(d["x"], d["norm"], f["gamma_f"], f.get("beta_f"), EPS,
+                                                             xq=d["xq"], x_scale=d["xs"]))
+        timer.run(f"gemm{i}", lambda: sq.sq_w8a8_gemm(d["xq"], d["xs"], f["wq"], f["w_scale"], y=d["y"],
+                                                      out_dtype=d["y"].dtype))
+
+
+def kernel_report(timer, wl, sites):
+    esize = {"f32": 4, "f16": 2, "bf16": 2}[wl.dtype]
+    osize = {"f32": 4, "f16": 2, "bf16": 2}[wl.out_dtype]
+    rep = {}
+    for i, d in enumerate(sites):
+        m, n, k = d["m"], d["n"], d["k"]
+        nparams = 0 if d["norm"] == "none" else (2 if d["norm"] == "layernorm" else 1)
+        t = timer.mean_ms(f"gemm{i}")
+        ops = 2.0 * m * n * k
+        gbytes = n * k + 4 * n + m * k + 4 * m + osize * m * n
+        rep[f"gemm{i}"] = {"shape": [m, n, k], "ms": t, "TOPS": ops / t / 1e9, "GBps": gbytes / t / 1e6}
+        t = timer.mean_ms(f"norm_quant{i}")
+        b = m * k * esize + m * k + 4 * m + 4 * k * (nparams if nparams else 1)
+        rep[f"norm_quant{i}"] = {"shape": [m, k], "ms": t, "GBps": b / t / 1e6}
+        t = timer.mean_ms(f"calibrate{i}")
+        b = wl.m_cal * k * esize + 4 * k
+        rep[f"calibrate{i}"] = {"shape": [wl.m_cal, k], "ms": t, "GBps": b / t / 1e6}
+        t = timer.mean_ms(f"fold{i}")
+        b = 2 * n * k * esize + n * k + 4 * n + 16 * k
+        rep[f"fold{i}"] = {"shape": [n, k], "ms": t, "GBps": b / t / 1e6}
+    return rep
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle on a bounded sample of the workload: every site's full chain on a few
+    tokens and output channels at the full K. Returns throughput in GEMM TOPS."""
+    import numpy as np
+    import oracle as O
+    from synth import site_inputs, to_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    m_s, n_s, cal_s = 4, 256, 16
+    elapsed = 0.0
+    ops = 0.0
+    reps = 0
+    while True:
+        for si, site in enumerate(wl.sites):
+            inp = site_inputs(wl.id, si, m=m_s, device="cpu", w_rows=n_s)
+            x = to_numpy(inp["x"])
+            x_cal = to_numpy(inp["x_cal"][:cal_s])
+            w = to_numpy(inp["w"])
+            gamma = None if inp["gamma"] is None else inp["gamma"].numpy()
+            beta = None if inp["beta"] is None else inp["beta"].numpy()
+            t0 = time.perf_counter()
+            O.w8a8_linear(x, x_cal, w, wl.dtype, site.norm, wl.alpha, gamma, beta, EPS, wl.out_dtype)
+            elapsed += time.perf_counter() - t0
+            ops += 2.0 * m_s * n_s * site.k
+        reps += 1
+        if elapsed >= budget_s or reps >= 50:
+            break
+    sample = (f"{reps} x every site's full oracle chain on {m_s} tokens, {cal_s} calibration tokens and the first "
+              f"{n_s} output channels at full K")
+    return {"value": ops / elapsed / 1e12, "unit": "TOPS", "cores": int(blas), "kind": "oracle", "sample": sample,
+            "seconds": elapsed, "note": "numpy, single-threaded except the BLAS matrix product"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import w8a8_int8_linear_amd as sq
+    from synth import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    m = args.m if args.m is not None else wl.m[0]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    print(f"# building inputs for {wl.name} (M={m})", file=sys.stderr, flush=True)
+    sites = build_sites(torch, sq, wl, m)
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        step(sq, wl, sites, timer)
+    torch.cuda.synchronize()
+    timer.reset()
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(sq, wl, sites, timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    ms = (t1 - t0) * 1e3 / args.steps
+    rep = kernel_report(timer, wl, sites)
+    gemm_ops = sum(2.0 * d["m"] * d["n"] * d["k"] for d in sites)
+    value = gemm_ops / (ms * 1e-3) / 1e12
+    g_ms = [rep[f"gemm{i}"]["ms"] for i in range(len(sites))]
+    g_ops = [2.0 * d["m"] * d["n"] * d["k"] for d in sites]
+    achieved = sum(g_ops) / (sum(g_ms) * 1e-3) / 1e12
+    out = {
+        "metric": "W8A8 GEMM TOPS + % INT8 MFMA peak; norm+quant kernel HBM GB/s",
+        "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8xint8->int32", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": m,
+                   "sites": [f"{s.name}: K={s.k} N={s.n} norm={s.norm}" for s in wl.sites],
+                   "alpha": wl.alpha, "act_dtype": wl.dtype, "out_dtype": wl.out_dtype, "m_cal": wl.m_cal},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_tile", "achieved": round(achieved, 1),
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None},
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in rep.items()},
+        "hbm_peak_GBps": PEAK_HBM_GBS,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/*
+ * smoothquant.h -- C ABI of the SmoothQuant W8A8 INT8 linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The calls follow the equivalent transform Y = X W = (X diag(s)^-1)(diag(s) W)
+ * ("LLM.int8() and SmoothQuant", section "Fix 2: move the difficulty into the
+ * weights"): offline, smoothquant_calibrate records the per-input-channel
+ * activation maxima and smoothquant_fold turns them into s, folds 1/s into the
+ * preceding norm and s into the weights, and quantises the weights per output
+ * channel; at run time sq_norm_quant applies the folded norm and quantises each
+ * token, and sq_w8a8_gemm multiplies the INT8 operands into INT32 and
+ * dequantises in its epilogue.
+ *
+ * Conventions shared by every call
+ *  - Every array argument is a DEVICE pointer owned by the caller. The library
+ *    allocates nothing, keeps no pointer after it returns and holds no state.
+ *  - Layouts are row-major and contiguous: activations [M, K], weights in the
+ *    torch Linear layout [N, K] (K, the input channel, is contiguous).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). A call
+ *    only enqueues kernels on it and returns; it never synchronises. Calls are
+ *    ordered by the stream. Outputs must not alias inputs.
+ *  - Every argument is validated before anything is launched; on an error the
+ *    call returns a non-zero sq_status and enqueues nothing. A launch failure
+ *    is reported as SQ_ERR_HIP. Faults during execution surface at the
+ *    caller's next synchronisation. NaN and Inf inputs are outside the contract.
+ *  - Shape limits: 1 <= M, N <= 2^31 - 1; 64 <= K <= SQ_K_MAX with K % 64 == 0
+ *    (SQ_K_MAX keeps |acc| <= K * 127^2 inside int32). Matrix pointers must be
+ *    16-byte aligned, vector pointers 4-byte aligned.
+ *  - The library is re-entrant and thread-safe: it has no global state.
+ *
+ * Number format readings (the pages state none of them): an INT8 step is
+ * fl32(absmax / 127) with IEEE division, codes are round-half-to-even of
+ * fl32(v / step) clipped to [-127, 127], and a zero step gives zero codes. Norm
+ * statistics are taken in binary64 and rounded once to binary32.
+ */
+#ifndef SMOOTHQUANT_H_
+#define SMOOTHQUANT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SQ_K_MAX 133120
+
+typedef enum {
+  SQ_OK = 0,
+  SQ_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
+  SQ_ERR_BAD_DTYPE = 2,     /* dtype not allowed for this argument */
+  SQ_ERR_BAD_SHAPE = 3,     /* M, N or K outside the limits above */
+  SQ_ERR_MISALIGNED = 4,    /* pointer alignment below the stated minimum */
+  SQ_ERR_BAD_ARG = 5,       /* alpha outside [0, 1], eps <= 0, unknown norm, illegal combination */
+  SQ_ERR_UNSUPPORTED = 6,   /* valid request this build does not implement */
+  SQ_ERR_HIP = 7            /* the HIP runtime refused a launch */
+} sq_status;
+
+typedef enum { SQ_DT_F32 = 0, SQ_DT_F16 = 1, SQ_DT_BF16 = 2, SQ_DT_I32 = 3 } sq_dtype;
+
+typedef enum { SQ_NORM_NONE = 0, SQ_NORM_LAYERNORM = 1, SQ_NORM_RMSNORM = 2 } sq_norm;
+
+/*
+ * Calibration absmax ("SmoothQuant, in depth", section "The calibration data
+ * flow": the running per-input-channel max of |x| at a linear's input over
+ * every calibration token).
+ *   x       [M, K] activations entering the norm, dtype x_dt in {F32, F16, BF16}.
+ *   norm    the norm in front of the linear. The recorded y is the norm output
+ *           with the UNFOLDED gamma/beta (LayerNorm: (x - mean) * rstd * gamma
+ *           + beta; RMSNorm: x * rstd * gamma), or x itself for SQ_NORM_NONE.
+ *   gamma   [K] fp32 or NULL (= 1); beta [K] fp32 or NULL (= 0, LayerNorm
+ *           only; must be NULL otherwise). Both are ignored for SQ_NORM_NONE.
+ *   eps     the norm's epsilon (> 0; unused for SQ_NORM_NONE).
+ *   absmax  [K] fp32 in/out: absmax[j] = max(absmax[j], max_t |y[t, j]|). The
+ *           caller zeroes it before the first batch; later calls keep the
+ *           running max.
+ */
+sq_status smoothquant_calibrate(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                sq_norm norm, const float* gamma, const float* beta, float eps,
+                                float* absmax, void* stream);
+
+/*
+ * Smoothing factors, fold and per-output-channel weight quantisation
+ * ("LLM.int8() and SmoothQuant", section "going deeper": s_j =
+ * max|X_j|^alpha / max|W_j|^(1-alpha); "SmoothQuant, in depth", its smoothing
+ * code: eps clamps on both maxima and on s, the norm weight and bias divided by
+ * s, each weight column multiplied by s; section "Where the scales go in a
+ * decoder block": q/k/v (or gate/up) share one s from the elementwise max of
+ * their weight maxima -- pass them concatenated along N to get exactly that).
+ *   act_absmax [K] fp32, from smoothquant_calibrate.
+ *   w          [N, K] weights, dtype w_dt in {F32, F16, BF16}.
+ *   alpha      migration strength in [0, 1] (binary64; the exponent of the
+ *              weight maximum is the binary64 value 1 - alpha).
+ *   eps        clamp (> 0), 1e-5 on the pages.
+ *   norm       the norm feeding these projections; gamma/beta are its
+ *              UNFOLDED parameters (NULL = 1 / 0, beta LayerNorm only).
+ * Outputs (all written):
+ *   s_out      [K] fp32: s_j = max(fl32(a'^alpha / w'^(1-alpha)), eps),
+ *              a' = max(act_absmax_j, eps), w' = max(max_n |W[n, j]|, eps),
+ *              the quotient evaluated in binary64 and rounded once.
+ *   gamma_out  [K] fp32: gamma / s (gamma NULL: 1 / s). For SQ_NORM_NONE it is
+ *              1 / s, the per-channel multiplier sq_norm_quant applies.
+ *   beta_out   [K] fp32: beta / s; required iff norm is LayerNorm and beta is
+ *              given, otherwise must be NULL.
+ *   wq         [N, K] int8: codes of W-hat = fl32(W * s) with one step per row.
+ *   w_scale    [N] fp32: fl32(max_j |W-hat[n, j]| / 127).
+ * s_out doubles as the buffer of the column maxima while the call runs.
+ */
+sq_status smoothquant_fold(const float* act_absmax, const void* w, sq_dtype w_dt,
+                           int64_t N, int64_t K, double alpha, float eps,
+                           sq_norm norm, const float* gamma, const float* beta,
+                           float* s_out, float* gamma_out, float* beta_out,
+                           int8_t* wq, float* w_scale, void* stream);
+
+/*
+ * Fused norm (with the folded gamma', beta') and per-token dynamic INT8
+ * quantisation ("LLM.int8() and SmoothQuant", section "Fix 2": the division by
+ * s is folded into the norm's weights so it costs nothing at run time;
+ * "SmoothQuant, in depth", section "Granularity: O1, O2, O3 ...": per-token
+ * dynamic activation scales).
+ *   x        [M, K] activations, dtype x_dt in {F32, F16, BF16}.
+ *   norm     LayerNorm: y = fl32(fl32(fl32(fl32(x - mean) * rstd) * gamma_f) + beta_f);
+ *            RMSNorm:   y = fl32(fl32(x * rstd) * gamma_f);
+ *            NONE:      y = fl32(x * gamma_f) (gamma_f NULL: y = x),
+ *            rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
+ *   gamma_f  [K] fp32 or NULL (= 1); beta_f [K] fp32 or NULL (LayerNorm only).
+ *   eps      the norm's epsilon (> 0; unused for SQ_NORM_NONE).
+ *   xq       [M, K] int8 out: codes of y with one step per row.
+ *   x_scale  [M] fp32 out: fl32(max_j |y[m, j]| / 127).
+ */
+sq_status sq_norm_quant(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                        sq_norm norm, const float* gamma_f, const float* beta_f, float eps,
+                        int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * INT8 x INT8 -> INT32 GEMM with the dequantising epilogue ("SmoothQuant, in
+ * depth", section "Granularity: O1, O2, O3 ...": out = acc * scale_token[i] *
+ * scale_channel[j], then conversion to FP16 or BF16).
+ *   xq [M, K] int8, x_scale [M] fp32; wq [N, K] int8, w_scale [N] fp32.
+ *   bias    [N] fp32 or NULL.
+ *   y       [M, N] out, dtype y_dt:
+ *           F32/F16/BF16: cvt(fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n]) (+ bias[n])),
+ *                         round-half-to-even into the output type;
+ *           I32: the raw accumulator acc[m, n] = sum_k xq[m, k] * wq[n, k]
+ *                (scales and bias must be NULL or are ignored).
+ */
+sq_status sq_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                       const float* bias, void* y, sq_dtype y_dt,
+                       int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* sq_status_string(sq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOOTHQUANT_H_ */

@@ -274,9 +274,13 @@ def calibrate(x, dtype, norm, gamma=None, beta=None, eps=1e-5, absmax=None):
 
 # --------------------------------------------------------------------------- O2 smoothing factors and fold
 
-def weight_colmax(w, dtype) -> np.ndarray:
-    """w_j = max over output rows n of |W[n, j]| for a torch-layout [N, K] weight."""
-    return np.max(np.abs(widen(w, dtype)), axis=0).astype(F32)
+def weight_colmax(w, dtype, block: int = 4096) -> np.ndarray:
+    """w_j = max over output rows n of |W[n, j]| for a torch-layout [N, K] weight (in row blocks)."""
+    w = np.asarray(w)
+    out = np.zeros(w.shape[1], F32)
+    for n0 in range(0, w.shape[0], block):
+        out = np.maximum(out, np.max(np.abs(widen(w[n0:n0 + block], dtype)), axis=0))
+    return out.astype(F32)
 
 
 def _s_exact(a: float, w: float, alpha: float):

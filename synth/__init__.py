@@ -14,4 +14,8 @@ from .workloads import (  # noqa: F401
     weight_block,
     outlier_channels,
     to_numpy,
+    rand_tokens,
+    rand_int8,
+    rand_positive,
+    norm_params,
 )

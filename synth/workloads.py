@@ -129,16 +129,24 @@ def calibration_block(wl: Workload, site_idx: int, device="cpu") -> torch.Tensor
     return _activations(wl, site_idx, wl.m_cal, "calib", device)
 
 
-def weight_block(wl: Workload, site_idx: int, device="cpu") -> torch.Tensor:
-    """Concatenated projection weights ``[N, K]`` (torch Linear layout), sigma as stated."""
+def weight_block(wl: Workload, site_idx: int, device="cpu", rows: int | None = None) -> torch.Tensor:
+    """Concatenated projection weights ``[N, K]`` (torch Linear layout), sigma as stated.
+
+    ``rows`` draws only that many output channels of the first projection (a
+    smaller sample with the same distribution, for host-side baselines).
+    """
     site = wl.sites[site_idx]
     parts = []
     for j, (_, n_out) in enumerate(site.parts):
+        if rows is not None:
+            n_out = rows
         g = _gen(_seed(wl.id, site_idx, "weights", j), device)
         w = torch.randn(n_out, site.k, generator=g, device=device, dtype=torch.float32)
         w *= site.w_sigma
         parts.append(w.to(DTYPES[wl.dtype]))
         del w
+        if rows is not None:
+            break
     return parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
 
 
@@ -156,7 +164,7 @@ def norm_params(wl: Workload, site_idx: int, device="cpu"):
     return gamma, beta
 
 
-def site_inputs(wl_id: int, site_idx: int, m: int | None = None, device="cpu") -> dict:
+def site_inputs(wl_id: int, site_idx: int, m: int | None = None, device="cpu", w_rows: int | None = None) -> dict:
     """Everything one site needs: runtime tokens, calibration tokens, weights, norm params."""
     wl = WORKLOADS[wl_id]
     site = wl.sites[site_idx]
@@ -164,7 +172,7 @@ def site_inputs(wl_id: int, site_idx: int, m: int | None = None, device="cpu") -
     gamma, beta = norm_params(wl, site_idx, device)
     return {
         "workload": wl, "site": site, "x": token_block(wl, site_idx, m, device),
-        "x_cal": calibration_block(wl, site_idx, device), "w": weight_block(wl, site_idx, device),
+        "x_cal": calibration_block(wl, site_idx, device), "w": weight_block(wl, site_idx, device, w_rows),
         "gamma": gamma, "beta": beta, "outliers": outlier_channels(wl, site_idx),
     }
 
@@ -175,3 +183,34 @@ def to_numpy(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+# ----------------------------------------------------------------------------- ad-hoc seeded tensors
+
+def rand_tokens(m: int, k: int, dtype: str, seed: int, n_outliers: int = 0, outlier_scale: float = 50.0,
+                dist: str = "normal", mean: float = 0.0, scale: float = 1.0) -> torch.Tensor:
+    """[m, k] activations on the CPU: N(mean, scale) (or Student-t(4)) with optional persistent outliers."""
+    g = _gen(seed, "cpu")
+    x = torch.randn(m, k, generator=g, dtype=torch.float32)
+    if dist == "student_t4":
+        u = torch.rand(2, m, k, generator=g, dtype=torch.float32)
+        e = -torch.log1p(-u)
+        x = x / torch.sqrt((e[0] + e[1]) * 0.5)
+    x = x * scale + mean
+    if n_outliers:
+        cols = torch.randperm(k, generator=g)[:n_outliers]
+        x[:, cols] *= outlier_scale
+    return x.to(DTYPES[dtype])
+
+
+def rand_int8(shape, seed: int, lo: int = -127, hi: int = 127) -> torch.Tensor:
+    """Uniform int8 codes in [lo, hi] on the CPU."""
+    g = _gen(seed, "cpu")
+    return torch.randint(lo, hi + 1, tuple(shape), generator=g, dtype=torch.int16).to(torch.int8)
+
+
+def rand_positive(n: int, seed: int, lo: float = 1e-3, hi: float = 1.0) -> torch.Tensor:
+    """n fp32 values log-uniform in [lo, hi] (per-row / per-channel INT8 steps)."""
+    g = _gen(seed, "cpu")
+    u = torch.rand(n, generator=g, dtype=torch.float64)
+    return torch.exp(np.log(lo) + u * (np.log(hi) - np.log(lo))).to(torch.float32)

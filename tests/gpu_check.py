@@ -1,0 +1,108 @@
+"""Comparison helpers for the GPU parity tests: the HIP results against the oracle.
+
+Integer codes, steps and accumulators must match bit for bit. Where the oracle
+reports a near-tie (a norm statistic or a smoothing factor whose exact value
+lies within a tiny distance of a binary32 rounding boundary), either neighbour
+is a correct rounding: the check accepts the GPU's choice only if it is one of
+the two candidates the oracle computed, and continues with that candidate.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from synth import to_numpy
+
+F32 = np.float32
+
+
+def bits(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16) if a.dtype.itemsize == 2 else a
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return to_numpy(t)
+
+
+def check_norm_quant(x_np, dtype, norm, gamma_f, beta_f, eps, xq_gpu, xs_gpu, label=""):
+    """Codes and steps of every row bit-exact; near-tie rows may take either statistic rounding."""
+    q, step, info = O.norm_quant(x_np, dtype, norm, gamma_f, beta_f, eps)
+    xq_gpu = np.asarray(xq_gpu)
+    xs_gpu = np.asarray(xs_gpu, F32)
+    bad = np.where((q != xq_gpu).any(axis=1) | (bits(step) != bits(xs_gpu)))[0]
+    ties = 0
+    for r in bad:
+        assert info["near_tie"][r], (
+            f"{label}: row {r} differs (step {step[r]!r} vs {xs_gpu[r]!r}, "
+            f"{int((q[r] != xq_gpu[r]).sum())} codes)")
+        variants = O.norm_quant_row_variants(x_np[r], dtype, norm, gamma_f, beta_f, eps)
+        assert any(np.array_equal(vq[0], xq_gpu[r]) and bits(vs)[0] == bits(xs_gpu[r:r + 1])[0]
+                   for vq, vs in variants), f"{label}: near-tie row {r} matches no correct rounding"
+        ties += 1
+    return ties
+
+
+def check_calibrate(x_np, dtype, norm, gamma, beta, eps, amax_gpu, prior=None, label=""):
+    a, info = O.calibrate(x_np, dtype, norm, gamma, beta, eps, absmax=prior)
+    amax_gpu = np.asarray(amax_gpu, F32)
+    diff = bits(a) != bits(amax_gpu)
+    if diff.any():
+        # a channel may take its max from a near-tie row evaluated with the other statistic rounding
+        tie_rows = np.where(info["near_tie"])[0]
+        assert len(tie_rows), f"{label}: {int(diff.sum())} channels differ with no near-tie row"
+        cands = [a]
+        for r in tie_rows:
+            st = info["alt"][r]
+            for mu in {float(st["mu"]), float(st["mu_other"])}:
+                for var in {float(st["var"]), float(st["var_other"])}:
+                    y = O.normalize(O.widen(x_np[r:r + 1], dtype), norm, [mu], [var], gamma, beta, eps)
+                    cands.append(np.abs(y[0]).astype(F32))
+        ok = np.any(bits(np.stack(cands)) == bits(amax_gpu)[None, :], axis=0)
+        assert ok[diff].all(), f"{label}: channels {np.where(diff & ~ok)[0][:8]} differ"
+    return a
+
+
+def check_fold(a_ref, w_np, dtype, alpha, eps, norm, gamma, beta, out_gpu, rows=None, label=""):
+    """s, gamma', beta' over all channels; codes and steps of W rows `rows` (all rows by default).
+
+    out_gpu holds the HIP results; with `rows`, out_gpu["wq"] / ["w_scale"] may be
+    just those rows (already gathered on the device).
+    """
+    s_ref, dist, other = O.smoothing_factors(a_ref, O.weight_colmax(w_np, dtype), alpha, eps)
+    s_gpu = host(out_gpu["s"])
+    diff = bits(s_ref) != bits(s_gpu)
+    if diff.any():
+        tie = dist < O.smoothquant_oracle.NEAR_TIE
+        other_ok = bits(other) == bits(s_gpu)
+        assert (tie & other_ok)[diff].all(), f"{label}: s differs at {np.where(diff & ~(tie & other_ok))[0][:8]}"
+        s_ref = np.where(diff, other, s_ref)
+    w_sel = w_np if rows is None else w_np[rows]
+    f = O.fold(a_ref, w_sel, dtype, alpha, eps, norm, gamma, beta, s=s_ref)
+    assert np.array_equal(bits(f["gamma_f"]), bits(host(out_gpu["gamma_f"]))), f"{label}: gamma' differs"
+    if f["beta_f"] is not None:
+        assert np.array_equal(bits(f["beta_f"]), bits(host(out_gpu["beta_f"]))), f"{label}: beta' differs"
+    wq_gpu = host(out_gpu["wq"])
+    ws_gpu = host(out_gpu["w_scale"])
+    if rows is not None and wq_gpu.shape[0] != len(rows):
+        wq_gpu, ws_gpu = wq_gpu[rows], ws_gpu[rows]
+    bad_rows = np.where((f["wq"] != wq_gpu).any(axis=1))[0]
+    assert not len(bad_rows), f"{label}: weight codes differ in rows {bad_rows[:8]}"
+    assert np.array_equal(bits(f["w_scale"]), bits(ws_gpu)), f"{label}: w_scale differs"
+    return f, int(diff.sum())
+
+
+def check_output(y_gpu_np, out_ref, v32_ref, out_dtype, label=""):
+    """Output within the stated tolerance, and (the epilogue order being pinned) bit-identical."""
+    if out_dtype == "bf16":
+        y = (y_gpu_np.astype(np.uint32) << 16).view(np.float32)
+    else:
+        y = y_gpu_np.astype(np.float32)
+    ref = v32_ref.astype(np.float64)
+    half_ulp_min = {"f32": 2.0 ** -150, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}[out_dtype]
+    err = np.abs(y.astype(np.float64) - ref)
+    tol = 2e-3 * np.abs(ref) + half_ulp_min
+    assert np.all(err <= tol), f"{label}: max rel err {np.max(err / np.maximum(np.abs(ref), 1e-30)):.3g}"
+    exact = np.mean(bits(np.ascontiguousarray(y_gpu_np)) == bits(np.ascontiguousarray(out_ref)))
+    assert exact == 1.0, f"{label}: {100 * (1 - exact):.4f}% of outputs not bit-identical"

@@ -1,0 +1,85 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry point
+include/smoothquant.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_int8_linear_amd as sq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "smoothquant.h")
+L = sq.lib
+F = ctypes.c_float
+A = ctypes.c_void_p(1 << 20)          # a 16-byte aligned non-null stand-in pointer (never dereferenced)
+A4 = ctypes.c_void_p((1 << 20) + 4)   # 4-byte aligned, not 16-byte aligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^(?:sq_status|const char\*)\s+(\w+)\s*\(", text, re.M))
+
+
+def test_header_declares_the_four_calls():
+    assert _declared() == {"smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
+                           "sq_status_string"}
+
+
+def test_library_exports_every_declared_symbol():
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert set(sq.EXPORTS) == _declared()
+
+
+def test_status_strings():
+    for code in range(8):
+        s = sq.status_string(code)
+        assert s.startswith("SQ_")
+    assert sq.status_string(0) == "SQ_OK"
+    assert "unknown" in sq.status_string(99)
+
+
+def nq(x=A, dt=1, m=16, k=512, norm=0, g=None, b=None, eps=1e-5, xq=A, xs=A):
+    return L.sq_norm_quant(x, dt, m, k, norm, g, b, F(eps), xq, xs, None)
+
+
+def gemm(xq=A, xs=A, wq=A, ws=A, bias=None, y=A, ydt=1, m=16, n=16, k=64):
+    return L.sq_w8a8_gemm(xq, xs, wq, ws, bias, y, ydt, m, n, k, None)
+
+
+def cal(x=A, dt=1, m=16, k=512, norm=1, g=None, b=None, eps=1e-5, amax=A):
+    return L.smoothquant_calibrate(x, dt, m, k, norm, g, b, F(eps), amax, None)
+
+
+def fold(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=None, s=A, go=A, bo=None,
+         wq=A, ws=A):
+    return L.smoothquant_fold(a, w, dt, n, k, ctypes.c_double(alpha), F(eps), norm, g, b, s, go, bo, wq, ws, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: nq(x=None), 1), (lambda: nq(xq=None), 1), (lambda: nq(xs=None), 1),
+    (lambda: nq(dt=3), 2), (lambda: nq(dt=7), 2),
+    (lambda: nq(m=0), 3), (lambda: nq(k=0), 3), (lambda: nq(k=100), 3), (lambda: nq(k=133184), 3),
+    (lambda: nq(m=1 << 31), 3),
+    (lambda: nq(x=A4), 4), (lambda: nq(xq=A4), 4), (lambda: nq(g=ctypes.c_void_p((1 << 20) + 2)), 4),
+    (lambda: nq(norm=5), 5), (lambda: nq(norm=2, b=A), 5), (lambda: nq(norm=0, b=A), 5),
+    (lambda: nq(norm=1, eps=0.0), 5), (lambda: nq(norm=2, eps=-1.0), 5),
+    (lambda: gemm(xq=None), 1), (lambda: gemm(y=None), 1), (lambda: gemm(xs=None), 1), (lambda: gemm(ws=None), 1),
+    (lambda: gemm(ydt=9), 2), (lambda: gemm(k=32), 3), (lambda: gemm(n=0), 3), (lambda: gemm(k=133120 + 64), 3),
+    (lambda: gemm(y=A4), 4), (lambda: gemm(wq=A4), 4),
+    (lambda: cal(x=None), 1), (lambda: cal(amax=None), 1), (lambda: cal(dt=3), 2), (lambda: cal(k=96), 3),
+    (lambda: cal(norm=9), 5), (lambda: cal(norm=2, b=A), 5), (lambda: cal(eps=0.0), 5), (lambda: cal(x=A4), 4),
+    (lambda: fold(a=None), 1), (lambda: fold(wq=None), 1), (lambda: fold(s=None), 1), (lambda: fold(go=None), 1),
+    (lambda: fold(dt=3), 2), (lambda: fold(n=0), 3), (lambda: fold(k=65), 3),
+    (lambda: fold(alpha=-0.1), 5), (lambda: fold(alpha=1.5), 5), (lambda: fold(alpha=float("nan")), 5),
+    (lambda: fold(eps=0.0), 5), (lambda: fold(norm=0, g=A), 5), (lambda: fold(norm=2, b=A, bo=A), 5),
+    (lambda: fold(b=A, bo=None), 1), (lambda: fold(b=None, bo=A), 5), (lambda: fold(w=A4), 4),
+])
+def test_bad_arguments_are_rejected_before_launch(call, code):
+    assert call() == code
+
+
+def test_gemm_i32_mode_accepts_null_scales():
+    # Validation passes (status would come from the launch); here only the argument check is exercised
+    # through a shape error raised after the scale checks.
+    assert gemm(xs=None, ws=None, ydt=3, k=65) == 3

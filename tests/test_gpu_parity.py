@@ -1,0 +1,182 @@
+"""HIP path against the oracle, stage by stage, on seeded inputs (needs an MI355X).
+
+Every stage gets the oracle's own inputs for that stage; codes, steps, smoothing
+factors and INT32 accumulators are compared bit for bit, dequantised outputs
+within 2e-3 relative (and, the epilogue order being pinned, bit-identical).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import w8a8_int8_linear_amd as sq
+from synth import rand_int8, rand_positive, rand_tokens, to_numpy
+from tests.gpu_check import bits, check_calibrate, check_fold, check_norm_quant, check_output, host
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+OUT_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}
+
+
+def _seed(*parts):
+    return zlib.crc32("/".join(map(str, parts)).encode()) & 0xFFFFF
+
+
+def cuda(t):
+    return None if t is None else t.to("cuda")
+
+
+def params(k, seed, norm):
+    g = torch.Generator().manual_seed(seed)
+    gamma = (1 + 0.1 * torch.randn(k, generator=g)).float()
+    beta = (0.1 * torch.randn(k, generator=g)).float() if norm == "layernorm" else None
+    return gamma, beta
+
+
+def np_or_none(t):
+    return None if t is None else t.numpy()
+
+
+# --------------------------------------------------------------------------- fused norm + quantise
+
+NQ_SHAPES = [(1, 64), (7, 512), (33, 4096), (5, 9216), (3, 20480), (2, 81920), (2, 133120)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("norm", ["none", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("shape", NQ_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_norm_quant(dtype, norm, shape):
+    m, k = shape
+    seed = _seed("nq", dtype, norm, m, k)
+    x = rand_tokens(m, k, dtype, seed, n_outliers=max(1, k // 1000), outlier_scale=60.0,
+                    mean=0.5 if norm == "layernorm" else 0.0)
+    gamma, beta = params(k, seed + 1, norm)
+    xq, xs = sq.sq_norm_quant(cuda(x), norm, cuda(gamma), cuda(beta), 1e-5)
+    torch.cuda.synchronize()
+    check_norm_quant(to_numpy(x), dtype, norm, np_or_none(gamma), np_or_none(beta), 1e-5, host(xq), host(xs),
+                     label=f"{dtype}/{norm}/{m}x{k}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_norm_quant_edge_rows(dtype):
+    k = 512
+    x = torch.zeros(8, k, dtype=torch.float32)
+    x[1] = -0.0                                             # signed zeros: step 0, codes 0
+    x[2, ::2], x[2, 1::2] = 2.5, -3.5                       # with absmax 127 below the step is exactly 1
+    x[2, 0] = 127.0
+    x[3] = torch.linspace(-1, 1, k) * 1e-30                 # tiny values
+    x[4] = torch.linspace(-1, 1, k) * 3e4                   # large values
+    x[5, 17] = -5.0                                          # a single nonzero
+    x[6] = 1.0                                               # constant row (LayerNorm variance 0)
+    x[7] = torch.arange(k) % 255 - 127                      # every code value
+    x = x.to(TORCH_DT[dtype])
+    for norm in ["none", "layernorm", "rmsnorm"]:
+        xq, xs = sq.sq_norm_quant(cuda(x), norm, None, None, 1e-5)
+        torch.cuda.synchronize()
+        check_norm_quant(to_numpy(x), dtype, norm, None, None, 1e-5, host(xq), host(xs), label=f"edge/{dtype}/{norm}")
+    q = host(sq.sq_norm_quant(cuda(x), "none")[0])
+    assert q[2, :4].tolist() == [127, -4, 2, -4] and not q[0].any() and not q[1].any()
+
+
+def test_norm_quant_repeatable():
+    x = cuda(rand_tokens(64, 4096, "f16", 5, n_outliers=4))
+    g, b = params(4096, 6, "layernorm")
+    r1 = sq.sq_norm_quant(x, "layernorm", cuda(g), cuda(b))
+    r2 = sq.sq_norm_quant(x, "layernorm", cuda(g), cuda(b))
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+# --------------------------------------------------------------------------- calibration
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("norm", ["none", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("shape", [(1, 64), (5, 4096), (64, 512), (513, 1024), (7, 20480)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_calibrate(dtype, norm, shape):
+    m, k = shape
+    seed = _seed("cal", dtype, norm, m, k)
+    x = rand_tokens(m, k, dtype, seed, n_outliers=3, outlier_scale=40.0)
+    gamma, beta = params(k, seed + 1, norm)
+    a = sq.smoothquant_calibrate(cuda(x), norm, cuda(gamma), cuda(beta), 1e-5)
+    torch.cuda.synchronize()
+    a_ref = check_calibrate(to_numpy(x), dtype, norm, np_or_none(gamma), np_or_none(beta), 1e-5, host(a),
+                            label=f"{dtype}/{norm}/{m}x{k}")
+    # a second batch keeps the running max
+    x2 = rand_tokens(m, k, dtype, seed + 2, n_outliers=3, outlier_scale=40.0)
+    sq.smoothquant_calibrate(cuda(x2), norm, cuda(gamma), cuda(beta), 1e-5, absmax=a)
+    torch.cuda.synchronize()
+    check_calibrate(to_numpy(x2), dtype, norm, np_or_none(gamma), np_or_none(beta), 1e-5, host(a), prior=a_ref,
+                    label=f"running/{dtype}/{norm}")
+
+
+# --------------------------------------------------------------------------- fold
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("norm", ["none", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 0.8, 1.0])
+@pytest.mark.parametrize("nk", [(1, 64), (17, 512), (300, 4096)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_fold(dtype, norm, alpha, nk):
+    n, k = nk
+    seed = _seed("fold", dtype, norm, alpha, n, k)
+    w = (rand_tokens(n, k, "f32", seed) * 0.02)
+    w[:, 3] = 0.0                                           # a dead input channel hits the eps clamp
+    w = w.to(TORCH_DT[dtype])
+    act = torch.abs(rand_tokens(1, k, "f32", seed + 1, n_outliers=2, outlier_scale=60.0))[0]
+    act[5] = 0.0
+    gamma, beta = params(k, seed + 2, norm)
+    if norm == "none":
+        gamma = beta = None
+    out = sq.smoothquant_fold(cuda(act), cuda(w), alpha, 1e-5, norm, cuda(gamma), cuda(beta))
+    torch.cuda.synchronize()
+    check_fold(act.numpy(), to_numpy(w), dtype, alpha, 1e-5, norm, np_or_none(gamma), np_or_none(beta), out,
+               label=f"{dtype}/{norm}/a{alpha}/{n}x{k}")
+
+
+# --------------------------------------------------------------------------- GEMM
+
+GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 1024), (65, 64, 64),
+               (256, 256, 128), (300, 520, 192), (513, 257, 640), (1000, 1000, 1088), (2, 9216, 9216),
+               (600, 700, 4096)]
+
+
+@pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_i32_exact(mnk):
+    m, n, k = mnk
+    xq = rand_int8((m, k), 100 + m)
+    wq = rand_int8((n, k), 200 + n)
+    acc = sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    ref = O.int_gemm(xq.numpy(), wq.numpy())
+    got = host(acc).astype(np.int64)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
+
+
+def test_gemm_int32_range_at_max_k():
+    k = sq.SQ_K_MAX
+    for m in [3, 70]:                                        # skinny and tiled kernels
+        xq = torch.full((m, k), 127, dtype=torch.int8)
+        xq[1] = -127
+        wq = torch.full((5, k), 127, dtype=torch.int8)
+        wq[2] = -127
+        acc = host(sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)).astype(np.int64)
+        assert np.array_equal(acc, O.int_gemm(xq.numpy(), wq.numpy()))
+        assert acc.max() == k * 127 * 127
+
+
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("mnk", [(1, 72, 64), (40, 300, 512), (300, 520, 192), (777, 1030, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_dequant(out, bias, mnk):
+    m, n, k = mnk
+    xq, wq = rand_int8((m, k), 300 + m), rand_int8((n, k), 400 + n)
+    xs, ws = rand_positive(m, 500 + m, 1e-3, 0.5), rand_positive(n, 600 + n, 1e-4, 0.05)
+    b = (rand_tokens(1, n, "f32", 700 + n)[0]) if bias else None
+    y = sq.sq_w8a8_gemm(cuda(xq), cuda(xs), cuda(wq), cuda(ws), cuda(b), out_dtype=OUT_DT[out])
+    torch.cuda.synchronize()
+    acc = O.int_gemm(xq.numpy(), wq.numpy())
+    out_ref, v32 = O.dequantize(acc, xs.numpy(), ws.numpy(), None if b is None else b.numpy(), out)
+    check_output(host(y), out_ref, v32, out, label=f"{out}/{m}x{n}x{k}")

@@ -1,0 +1,24 @@
+"""SmoothQuant W8A8 INT8 linear layer for AMD Instinct MI355X (gfx950).
+
+The compute lives in libsmoothquant.so (hand-written HIP kernels behind a C
+ABI, declared in include/smoothquant.h); this package only binds it.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    SQ_DT_BF16,
+    SQ_DT_F16,
+    SQ_DT_F32,
+    SQ_DT_I32,
+    SQ_K_MAX,
+    SQ_NORM_LAYERNORM,
+    SQ_NORM_NONE,
+    SQ_NORM_RMSNORM,
+    SmoothQuantError,
+    lib,
+    smoothquant_calibrate,
+    smoothquant_fold,
+    sq_norm_quant,
+    sq_w8a8_gemm,
+    status_string,
+)

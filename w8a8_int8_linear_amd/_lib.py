@@ -1,0 +1,173 @@
+"""ctypes binding of libsmoothquant.so (argument marshalling only).
+
+Each wrapper takes torch tensors for their device memory and the current HIP
+stream, checks shapes and dtypes, and calls the C entry point of the same
+name. Every computation runs in the library's HIP kernels; there is no
+fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmoothquant.so")
+
+SQ_OK = 0
+SQ_DT_F32, SQ_DT_F16, SQ_DT_BF16, SQ_DT_I32 = 0, 1, 2, 3
+SQ_NORM_NONE, SQ_NORM_LAYERNORM, SQ_NORM_RMSNORM = 0, 1, 2
+SQ_K_MAX = 133120
+
+_DT = {torch.float32: SQ_DT_F32, torch.float16: SQ_DT_F16, torch.bfloat16: SQ_DT_BF16, torch.int32: SQ_DT_I32}
+_NORM = {"none": SQ_NORM_NONE, "layernorm": SQ_NORM_LAYERNORM, "rmsnorm": SQ_NORM_RMSNORM,
+         SQ_NORM_NONE: SQ_NORM_NONE, SQ_NORM_LAYERNORM: SQ_NORM_LAYERNORM, SQ_NORM_RMSNORM: SQ_NORM_RMSNORM}
+
+EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm", "sq_status_string")
+
+
+class SmoothQuantError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m w8a8_int8_linear_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, F, D, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_int
+    lib.smoothquant_calibrate.argtypes = [P, I, I64, I64, I, P, P, F, P, P]
+    lib.smoothquant_fold.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
+    lib.sq_norm_quant.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P]
+    lib.sq_w8a8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.sq_status_string.argtypes = [I]
+    lib.sq_status_string.restype = ctypes.c_char_p
+    for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = I
+    return lib
+
+
+lib = load_library()
+
+
+def status_string(status: int) -> str:
+    return lib.sq_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _check(fn: str, status: int):
+    if status != SQ_OK:
+        raise SmoothQuantError(fn, status)
+
+
+_ACT = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def smoothquant_calibrate(x, norm="none", gamma=None, beta=None, eps=1e-5, absmax=None):
+    """Running per-channel max of |norm(x)| into absmax [K] fp32 (created zeroed if None)."""
+    _dev(x, "x", _ACT)
+    m, k = x.shape
+    if absmax is None:
+        absmax = torch.zeros(k, dtype=torch.float32, device=x.device)
+    _dev(absmax, "absmax", torch.float32, (k,))
+    _dev(gamma, "gamma", torch.float32, (k,))
+    _dev(beta, "beta", torch.float32, (k,))
+    with torch.cuda.device(x.device):
+        _check("smoothquant_calibrate", lib.smoothquant_calibrate(
+            _ptr(x), _DT[x.dtype], m, k, _NORM[norm], _ptr(gamma), _ptr(beta), eps, _ptr(absmax), _stream(x)))
+    return absmax
+
+
+def smoothquant_fold(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, beta=None, out=None):
+    """Smoothing factors, folded norm parameters and INT8 weights for w [N, K].
+
+    Returns dict(s, gamma_f, beta_f, wq, w_scale); `out` may supply those buffers.
+    """
+    _dev(w, "w", _ACT)
+    n, k = w.shape
+    _dev(act_absmax, "act_absmax", torch.float32, (k,))
+    _dev(gamma, "gamma", torch.float32, (k,))
+    _dev(beta, "beta", torch.float32, (k,))
+    out = dict(out or {})
+    dev = w.device
+    out.setdefault("s", torch.empty(k, dtype=torch.float32, device=dev))
+    out.setdefault("gamma_f", torch.empty(k, dtype=torch.float32, device=dev))
+    if beta is not None:
+        out.setdefault("beta_f", torch.empty(k, dtype=torch.float32, device=dev))
+    else:
+        out["beta_f"] = None
+    out.setdefault("wq", torch.empty(n, k, dtype=torch.int8, device=dev))
+    out.setdefault("w_scale", torch.empty(n, dtype=torch.float32, device=dev))
+    for key, shp, dt in [("s", (k,), torch.float32), ("gamma_f", (k,), torch.float32),
+                         ("beta_f", (k,), torch.float32), ("wq", (n, k), torch.int8), ("w_scale", (n,), torch.float32)]:
+        _dev(out[key], key, dt, shp)
+    with torch.cuda.device(dev):
+        _check("smoothquant_fold", lib.smoothquant_fold(
+            _ptr(act_absmax), _ptr(w), _DT[w.dtype], n, k, float(alpha), eps, _NORM[norm], _ptr(gamma), _ptr(beta),
+            _ptr(out["s"]), _ptr(out["gamma_f"]), _ptr(out["beta_f"]), _ptr(out["wq"]), _ptr(out["w_scale"]),
+            _stream(w)))
+    return out
+
+
+def sq_norm_quant(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
+    """Fused norm (folded gamma', beta') + per-token INT8: returns (xq [M, K] int8, x_scale [M] fp32)."""
+    _dev(x, "x", _ACT)
+    m, k = x.shape
+    _dev(gamma_f, "gamma_f", torch.float32, (k,))
+    _dev(beta_f, "beta_f", torch.float32, (k,))
+    if xq is None:
+        xq = torch.empty(m, k, dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _dev(xq, "xq", torch.int8, (m, k))
+    _dev(x_scale, "x_scale", torch.float32, (m,))
+    with torch.cuda.device(x.device):
+        _check("sq_norm_quant", lib.sq_norm_quant(
+            _ptr(x), _DT[x.dtype], m, k, _NORM[norm], _ptr(gamma_f), _ptr(beta_f), eps, _ptr(xq), _ptr(x_scale),
+            _stream(x)))
+    return xq, x_scale
+
+
+def sq_w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.float16, y=None):
+    """y [M, N] = dequant(xq @ wq^T); out_dtype torch.int32 returns the raw accumulator."""
+    _dev(xq, "xq", torch.int8)
+    _dev(wq, "wq", torch.int8)
+    m, k = xq.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
+    if out_dtype != torch.int32:
+        _dev(x_scale, "x_scale", torch.float32, (m,))
+        _dev(w_scale, "w_scale", torch.float32, (n,))
+        _dev(bias, "bias", torch.float32, (n,))
+    if y is None:
+        y = torch.empty(m, n, dtype=out_dtype, device=xq.device)
+    _dev(y, "y", out_dtype, (m, n))
+    with torch.cuda.device(xq.device):
+        _check("sq_w8a8_gemm", lib.sq_w8a8_gemm(
+            _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DT[y.dtype], m, n, k,
+            _stream(xq)))
+    return y

@@ -1,0 +1,72 @@
+// C ABI entry points: validate every argument, then enqueue the kernels on the
+// caller's stream. Nothing here allocates, synchronises or keeps state.
+#include <hip/hip_runtime.h>
+
+#include "smoothquant.h"
+#include "sq_launch.h"
+#include "sq_validate.h"
+
+namespace {
+
+sq_status from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+sq_status smoothquant_calibrate(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm,
+                                const float* gamma, const float* beta, float eps, float* absmax, void* stream) {
+  if (sq_status s = sq::check_calibrate(x, x_dt, M, K, norm, gamma, beta, eps, absmax)) return s;
+  sq::RowArgs a{x, x_dt, M, static_cast<int>(K), norm,
+                norm == SQ_NORM_NONE ? nullptr : gamma, norm == SQ_NORM_LAYERNORM ? beta : nullptr,
+                eps, nullptr, nullptr, absmax};
+  return from_hip(sq::launch_calibrate(a, as_stream(stream)));
+}
+
+sq_status smoothquant_fold(const float* act_absmax, const void* w, sq_dtype w_dt, int64_t N, int64_t K,
+                           double alpha, float eps, sq_norm norm, const float* gamma, const float* beta,
+                           float* s_out, float* gamma_out, float* beta_out, int8_t* wq, float* w_scale,
+                           void* stream) {
+  if (sq_status s = sq::check_fold(act_absmax, w, w_dt, N, K, alpha, eps, norm, gamma, beta, s_out, gamma_out,
+                                   beta_out, wq, w_scale))
+    return s;
+  hipStream_t st = as_stream(stream);
+  sq::FoldArgs f{act_absmax, w, w_dt, N, K, alpha, eps, gamma, beta, s_out, gamma_out, beta_out};
+  if (sq_status s = from_hip(sq::launch_fold_colmax_scales(f, st))) return s;
+  // W-hat = fl32(W * s) quantised per output row: the NONE-norm quantiser with gamma = s.
+  sq::RowArgs q{w, w_dt, N, static_cast<int>(K), SQ_NORM_NONE, s_out, nullptr, 1.0f, wq, w_scale, nullptr};
+  return from_hip(sq::launch_norm_quant(q, st));
+}
+
+sq_status sq_norm_quant(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm, const float* gamma_f,
+                        const float* beta_f, float eps, int8_t* xq, float* x_scale, void* stream) {
+  if (sq_status s = sq::check_norm_quant(x, x_dt, M, K, norm, gamma_f, beta_f, eps, xq, x_scale)) return s;
+  sq::RowArgs a{x, x_dt, M, static_cast<int>(K), norm, gamma_f, beta_f, eps, xq, x_scale, nullptr};
+  return from_hip(sq::launch_norm_quant(a, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                       const float* bias, void* y, sq_dtype y_dt, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (sq_status s = sq::check_gemm(xq, x_scale, wq, w_scale, bias, y, y_dt, M, N, K)) return s;
+  sq::GemmArgs g{xq, x_scale, wq, w_scale, y_dt == SQ_DT_I32 ? nullptr : bias, y, y_dt,
+                 static_cast<int>(M), static_cast<int>(N), static_cast<int>(K)};
+  return from_hip(sq::launch_gemm(g, as_stream(stream)));
+}
+
+const char* sq_status_string(sq_status s) {
+  switch (s) {
+    case SQ_OK: return "SQ_OK";
+    case SQ_ERR_NULL_POINTER: return "SQ_ERR_NULL_POINTER: a required pointer is NULL";
+    case SQ_ERR_BAD_DTYPE: return "SQ_ERR_BAD_DTYPE: dtype not allowed for this argument";
+    case SQ_ERR_BAD_SHAPE: return "SQ_ERR_BAD_SHAPE: need 1 <= M, N < 2^31 and 64 <= K <= 133120 with K % 64 == 0";
+    case SQ_ERR_MISALIGNED: return "SQ_ERR_MISALIGNED: matrices need 16-byte, vectors 4-byte alignment";
+    case SQ_ERR_BAD_ARG: return "SQ_ERR_BAD_ARG: alpha, eps, norm or pointer combination not allowed";
+    case SQ_ERR_UNSUPPORTED: return "SQ_ERR_UNSUPPORTED: not implemented by this build";
+    case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime refused a launch";
+  }
+  return "unknown sq_status";
+}
+
+}  // extern "C"

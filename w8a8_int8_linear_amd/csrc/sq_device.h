@@ -1,0 +1,167 @@
+// Device helpers shared by the row kernels and the GEMM epilogues (gfx950, wave64).
+//
+// Every elementwise binary32 step below is written with the explicit
+// round-to-nearest intrinsics so that no multiply-add is ever contracted: the
+// library's numerical contract gives each operation its own rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <cstdint>
+
+namespace sq {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------------------- storage types
+struct f32_t {};
+struct f16_t {};
+struct bf16_t {};
+
+template <typename T> struct Storage;
+template <> struct Storage<f32_t> { static constexpr int kBytes = 4; };
+template <> struct Storage<f16_t> { static constexpr int kBytes = 2; };
+template <> struct Storage<bf16_t> { static constexpr int kBytes = 2; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
+}
+
+// Load 8 consecutive elements (p is 16-byte aligned) and widen them exactly to binary32.
+template <typename T> __device__ __forceinline__ void load8(const void* p, float v[8]);
+
+template <> __device__ __forceinline__ void load8<f32_t>(const void* p, float v[8]) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
+template <> __device__ __forceinline__ void load8<f16_t>(const void* p, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = f16_bits_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+template <> __device__ __forceinline__ void load8<bf16_t>(const void* p, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// ----------------------------------------------------------------------------- output conversion
+// binary32 -> bfloat16 bits, round half to even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(f)));
+}
+
+// ----------------------------------------------------------------------------- reductions
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Block-wide sum in a fixed order (deterministic run to run). `red` holds >= THREADS/64 doubles.
+template <int THREADS>
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  constexpr int kWaves = THREADS / kWave;
+  v = wave_sum(v);
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += red[i];
+  return t;
+}
+
+template <int THREADS>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  constexpr int kWaves = THREADS / kWave;
+  v = wave_max(v);
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// ----------------------------------------------------------------------------- INT8 codes
+// Step of a row: fl32(absmax / 127) with IEEE division.
+__device__ __forceinline__ float int8_step(float amax) { return __fdiv_rn(amax, 127.0f); }
+
+// Per-row quantiser: code = clip(rne(fl32(y / step)), -127, 127).
+//
+// The quotient fl32(y / step) is needed only to decide which side of a
+// half-integer it falls on. t = fl32(y * fl32(1 / step)) differs from the
+// exact quotient Q by at most |Q| * 2^-22.9 and fl32(Q) by less than
+// |Q| * 2^-22 <= 2^-15 (|Q| <= 128), so rne(t) = rne(fl32(Q)) whenever t lies
+// farther than 2^-15 from every half-integer. The rare elements inside that
+// band take the IEEE division. Steps below 2^-100 (where 1/step may overflow)
+// always divide.
+struct Quantizer {
+  float step, rcp;
+  bool zero, exact_only;
+  __device__ __forceinline__ explicit Quantizer(float st) : step(st) {
+    zero = !(st > 0.0f);
+    exact_only = st < 0x1p-100f;
+    rcp = zero ? 0.0f : __frcp_rn(st);
+  }
+  // Codes of 8 values, packed little-endian into two 32-bit words.
+  __device__ __forceinline__ uint2 codes8(const float y[8]) const {
+    float q[8];
+    bool slow = exact_only;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = __fmul_rn(y[i], rcp);
+      q[i] = rintf(t);
+      slow |= !(fabsf(__fsub_rn(t, q[i])) < 0.499969482421875f);  // 0.5 - 2^-15
+    }
+    if (slow) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = rintf(__fdiv_rn(y[i], step));
+    }
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = zero ? 0 : static_cast<int>(fminf(fmaxf(q[i], -127.0f), 127.0f));
+      const uint32_t b = static_cast<uint32_t>(c) & 0xffu;
+      if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
+    }
+    return make_uint2(w0, w1);
+  }
+};
+
+// Max over non-negative binary32 values through their bit patterns (IEEE order
+// equals unsigned order there), order-independent and exact.
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace sq

@@ -1,0 +1,58 @@
+// Host-side launchers of the HIP kernels (argument bundles already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "smoothquant.h"
+
+namespace sq {
+
+// norm + quantise (xq, x_scale) or calibration (absmax) over `rows` rows of K.
+struct RowArgs {
+  const void* x;
+  sq_dtype dtype;
+  int64_t rows;
+  int K;
+  sq_norm norm;
+  const float* gamma;
+  const float* beta;
+  float eps;
+  int8_t* xq;
+  float* x_scale;
+  float* absmax;
+};
+
+struct FoldArgs {
+  const float* act_absmax;
+  const void* w;
+  sq_dtype dtype;
+  int64_t N, K;
+  double alpha;
+  float eps;
+  const float* gamma;
+  const float* beta;
+  float* s_out;
+  float* gamma_out;
+  float* beta_out;
+};
+
+struct GemmArgs {
+  const int8_t* xq;
+  const float* x_scale;
+  const int8_t* wq;
+  const float* w_scale;
+  const float* bias;
+  void* y;
+  sq_dtype y_dt;
+  int M, N, K;
+};
+
+hipError_t launch_norm_quant(const RowArgs& a, hipStream_t st);
+hipError_t launch_calibrate(const RowArgs& a, hipStream_t st);
+// Column maxima of W into s_out, then s, gamma', beta' (the weight codes are a
+// norm_quant pass over W with gamma = s).
+hipError_t launch_fold_colmax_scales(const FoldArgs& f, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
+}  // namespace sq

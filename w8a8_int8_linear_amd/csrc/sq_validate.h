@@ -1,0 +1,27 @@
+// Argument checks of the C ABI. Pure C++ with no HIP calls: every check runs
+// on the host before anything is launched, so the error paths work (and can be
+// tested) on a machine without a GPU.
+#pragma once
+
+#include <cstdint>
+
+#include "smoothquant.h"
+
+namespace sq {
+
+sq_status check_calibrate(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm,
+                          const float* gamma, const float* beta, float eps, const float* absmax);
+
+sq_status check_fold(const float* act_absmax, const void* w, sq_dtype w_dt, int64_t N, int64_t K,
+                     double alpha, float eps, sq_norm norm, const float* gamma, const float* beta,
+                     const float* s_out, const float* gamma_out, const float* beta_out,
+                     const int8_t* wq, const float* w_scale);
+
+sq_status check_norm_quant(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm,
+                           const float* gamma_f, const float* beta_f, float eps,
+                           const int8_t* xq, const float* x_scale);
+
+sq_status check_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                     const float* bias, const void* y, sq_dtype y_dt, int64_t M, int64_t N, int64_t K);
+
+}  // namespace sq
