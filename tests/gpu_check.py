@@ -94,15 +94,24 @@ def check_fold(a_ref, w_np, dtype, alpha, eps, norm, gamma, beta, out_gpu, rows=
 
 
 def check_output(y_gpu_np, out_ref, v32_ref, out_dtype, label=""):
-    """Output within the stated tolerance, and (the epilogue order being pinned) bit-identical."""
-    if out_dtype == "bf16":
-        y = (y_gpu_np.astype(np.uint32) << 16).view(np.float32)
-    else:
-        y = y_gpu_np.astype(np.float32)
-    ref = v32_ref.astype(np.float64)
+    """Output within 2e-3 relative of the oracle's output in the same output type, and
+    (the epilogue order being pinned) bit-identical to it.
+
+    The bound is taken after both sides convert to the output type: bfloat16 keeps
+    8 significant bits, so its own rounding may move a value by up to 2^-8 of it,
+    more than 2e-3, while fp16 (2^-11) and fp32 stay well inside.
+    """
+    def as_f64(a):
+        a = np.ascontiguousarray(a)
+        if out_dtype == "bf16":
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+    y, ref = as_f64(y_gpu_np), as_f64(out_ref)
     half_ulp_min = {"f32": 2.0 ** -150, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}[out_dtype]
-    err = np.abs(y.astype(np.float64) - ref)
-    tol = 2e-3 * np.abs(ref) + half_ulp_min
-    assert np.all(err <= tol), f"{label}: max rel err {np.max(err / np.maximum(np.abs(ref), 1e-30)):.3g}"
+    err = np.abs(y - ref)
+    assert np.all(err <= 2e-3 * np.abs(ref) + half_ulp_min), (
+        f"{label}: max rel err {np.max(err / np.maximum(np.abs(ref), 1e-30)):.3g}")
+    u = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[out_dtype]
+    assert np.all(np.abs(ref - v32_ref.astype(np.float64)) <= u * np.abs(v32_ref.astype(np.float64)) + half_ulp_min)
     exact = np.mean(bits(np.ascontiguousarray(y_gpu_np)) == bits(np.ascontiguousarray(out_ref)))
     assert exact == 1.0, f"{label}: {100 * (1 - exact):.4f}% of outputs not bit-identical"

@@ -53,8 +53,8 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int nn = min(n + r, N - 1);
-      float t = __fmul_rn(__fmul_rn(static_cast<float>(acc[r]), xs), ws[nn]);
-      if (bias) t = __fadd_rn(t, bias[nn]);
+      float t = mul_rn(mul_rn(static_cast<float>(acc[r]), xs), ws[nn]);
+      if (bias) t = add_rn(t, bias[nn]);
       o[r] = t;
     }
     if constexpr (YDT == SQ_DT_F32) {

@@ -55,7 +55,7 @@ __device__ __forceinline__ void row_y(const char* __restrict__ xrow, int K, cons
     s2 = block_sum<THREADS>(s2, red);
     mu = static_cast<float>(mean);
     const float var = static_cast<float>(s2 / static_cast<double>(K));
-    r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(var, eps)));
+    r = div_rn(1.0f, sqrt_rn(add_rn(var, eps)));
   } else if constexpr (NORM == SQ_NORM_RMSNORM) {
     double s2 = 0.0;
 #pragma unroll
@@ -67,7 +67,7 @@ __device__ __forceinline__ void row_y(const char* __restrict__ xrow, int K, cons
       }
     s2 = block_sum<THREADS>(s2, red);
     const float var = static_cast<float>(s2 / static_cast<double>(K));
-    r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(var, eps)));
+    r = div_rn(1.0f, sqrt_rn(add_rn(var, eps)));
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -87,10 +87,10 @@ __device__ __forceinline__ void row_y(const char* __restrict__ xrow, int K, cons
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float t = v[i][e];
-      if constexpr (NORM == SQ_NORM_LAYERNORM) t = __fmul_rn(__fsub_rn(t, mu), r);
-      if constexpr (NORM == SQ_NORM_RMSNORM) t = __fmul_rn(t, r);
-      if (gamma) t = __fmul_rn(t, g[e]);
-      if (NORM == SQ_NORM_LAYERNORM && beta) t = __fadd_rn(t, b[e]);
+      if constexpr (NORM == SQ_NORM_LAYERNORM) t = mul_rn(sub_rn(t, mu), r);
+      if constexpr (NORM == SQ_NORM_RMSNORM) t = mul_rn(t, r);
+      if (gamma) t = mul_rn(t, g[e]);
+      if (NORM == SQ_NORM_LAYERNORM && beta) t = add_rn(t, b[e]);
       v[i][e] = t;
     }
   }
@@ -210,8 +210,8 @@ __global__ void k_scales(const float* __restrict__ act_absmax, float* __restrict
   const double q = pow(static_cast<double>(a1), alpha) / pow(static_cast<double>(w1), 1.0 - alpha);
   const float s = fmaxf(static_cast<float>(q), eps);
   s_io[j] = s;
-  gamma_out[j] = __fdiv_rn(gamma ? gamma[j] : 1.0f, s);
-  if (beta_out) beta_out[j] = __fdiv_rn(beta[j], s);
+  gamma_out[j] = div_rn(gamma ? gamma[j] : 1.0f, s);
+  if (beta_out) beta_out[j] = div_rn(beta[j], s);
 }
 
 // ----------------------------------------------------------------------------- launchers

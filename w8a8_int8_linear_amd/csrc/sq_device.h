@@ -1,9 +1,14 @@
 // Device helpers shared by the row kernels and the GEMM epilogues (gfx950, wave64).
 //
-// Every elementwise binary32 step below is written with the explicit
-// round-to-nearest intrinsics so that no multiply-add is ever contracted: the
-// library's numerical contract gives each operation its own rounding.
+// The library's numerical contract gives every binary32 operation its own
+// round-to-nearest-even rounding: no multiply-add is contracted (the pragma
+// below, also -ffp-contract=off on the command line), and division and square
+// root are the IEEE-correct ones (the HIP default,
+// -fhip-fp32-correctly-rounded-divide-sqrt). HIP's __fsqrt_rn is NOT used: it
+// maps to the approximate hardware square root unless the ocml rounded
+// operations are enabled.
 #pragma once
+#pragma clang fp contract(off)
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -12,6 +17,13 @@
 namespace sq {
 
 constexpr int kWave = 64;
+
+// Correctly rounded binary32 operations (see the header comment).
+__device__ __forceinline__ float add_rn(float a, float b) { return a + b; }
+__device__ __forceinline__ float sub_rn(float a, float b) { return a - b; }
+__device__ __forceinline__ float mul_rn(float a, float b) { return a * b; }
+__device__ __forceinline__ float div_rn(float a, float b) { return a / b; }
+__device__ __forceinline__ float sqrt_rn(float a) { return __builtin_sqrtf(a); }
 
 // ----------------------------------------------------------------------------- storage types
 struct f32_t {};
@@ -114,7 +126,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 // ----------------------------------------------------------------------------- INT8 codes
 // Step of a row: fl32(absmax / 127) with IEEE division.
-__device__ __forceinline__ float int8_step(float amax) { return __fdiv_rn(amax, 127.0f); }
+__device__ __forceinline__ float int8_step(float amax) { return div_rn(amax, 127.0f); }
 
 // Per-row quantiser: code = clip(rne(fl32(y / step)), -127, 127).
 //
@@ -131,7 +143,7 @@ struct Quantizer {
   __device__ __forceinline__ explicit Quantizer(float st) : step(st) {
     zero = !(st > 0.0f);
     exact_only = st < 0x1p-100f;
-    rcp = zero ? 0.0f : __frcp_rn(st);
+    rcp = zero ? 0.0f : div_rn(1.0f, st);
   }
   // Codes of 8 values, packed little-endian into two 32-bit words.
   __device__ __forceinline__ uint2 codes8(const float y[8]) const {
@@ -139,13 +151,13 @@ struct Quantizer {
     bool slow = exact_only;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float t = __fmul_rn(y[i], rcp);
+      const float t = mul_rn(y[i], rcp);
       q[i] = rintf(t);
-      slow |= !(fabsf(__fsub_rn(t, q[i])) < 0.499969482421875f);  // 0.5 - 2^-15
+      slow |= !(fabsf(sub_rn(t, q[i])) < 0.499969482421875f);  // 0.5 - 2^-15
     }
     if (slow) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = rintf(__fdiv_rn(y[i], step));
+      for (int i = 0; i < 8; ++i) q[i] = rintf(div_rn(y[i], step));
     }
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
