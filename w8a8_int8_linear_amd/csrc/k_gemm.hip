@@ -5,12 +5,13 @@
 //
 // Two kernels:
 //  * k_gemm_tile  -- prefill shapes. 256x256 output tile per workgroup of eight
-//    waves (2 x 4, 128 x 64 each: two waves per SIMD, accumulators in VGPRs), K staged through LDS in 128-byte slices with
-//    buffer->LDS DMA (buffer_load_dwordx4 ... lds) into a double buffer, computed
-//    with v_mfma_i32_16x16x64_i8. The LDS rows are XOR-swizzled in 16-byte
-//    chunks so the fragment reads are bank-conflict free. Workgroups are mapped
-//    to tiles XCD by XCD and in column groups, so tiles that share operand rows
-//    run at the same time on the same L2.
+//    waves (2 x 4, 128 x 64 each: two waves per SIMD, accumulators in VGPRs), K
+//    staged through LDS in 64-byte slices by buffer->LDS DMA
+//    (buffer_load_dwordx4 ... lds) into a 4-stage ring with three slices in
+//    flight, computed with v_mfma_i32_16x16x64_i8. LDS rows are swizzled in
+//    16-byte chunks so the fragment reads are bank-conflict free. Workgroups are
+//    mapped to tiles XCD by XCD and in column groups, so tiles that share
+//    operand rows run at the same time on the same L2.
 //  * k_gemm_skinny -- decode shapes (M <= 64), bound by streaming wq from HBM.
 //    A workgroup owns 16 output channels; its four waves split K, each streams
 //    its 16 rows of wq straight into MFMA operands and the partial accumulators
@@ -84,18 +85,22 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n
 
 // ----------------------------------------------------------------------------- tiled kernel
 
-constexpr int kTile = 256;        // output tile edge (m and n)
-constexpr int kSlice = 128;       // K bytes per LDS stage
-constexpr int kStageBytes = kTile * kSlice;   // one operand, one stage: 32 KiB
+constexpr int kTile = 256;                     // output tile edge (m and n)
+constexpr int kSlice = 64;                     // K bytes per LDS stage: one MFMA K step
+constexpr int kStages = 4;                     // LDS ring depth: slices in flight = kStages - 1
+constexpr int kStageBytes = kTile * kSlice;    // one operand, one stage: 16 KiB
+constexpr int kDmaPerWave = kStageBytes / 1024 / 8;   // 1 KiB DMA instructions per wave per operand: 2
 
-// 16-byte chunk position of chunk c in LDS row r (bank-conflict-free fragment
-// reads for both 8- and 16-lane access phases).
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// LDS layout of a stage: row r of the operand at r * 64, its 16-byte K chunk c
+// at slot c ^ swz(r). A ds_read_b128 serves 32 lanes at a time from a 512-byte
+// window; a fragment read has lanes 0..31 on 16 rows x 2 chunks, and rows r,
+// r + 8 share a window position, so they get slots differing in bit 1.
+__device__ __forceinline__ int swz(int r) { return ((r >> 3) & 1) << 1; }
 
 // Workgroup -> tile. Consecutive workgroup ids land on different XCDs (round
 // robin over 8), so ids are first regrouped so that each XCD receives a
 // contiguous range of tile numbers; tile numbers then walk `group` tile-rows
-// at a time, so concurrently running tiles share rows of xq and wq.
+// at a time, so concurrently running tiles share rows of xq and wq in L2.
 __device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int group, int& tm, int& tn) {
   const int q = nwg >> 3, rem = nwg & 7;
   const int xcd = bid & 7, idx = bid >> 3;
@@ -111,57 +116,80 @@ __device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int grou
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Workgroup barrier without the release/acquire fences of __syncthreads (those
+// would drain every outstanding DMA, vmcnt(0)). The memory clobber keeps the
+// compiler from moving LDS accesses across it; visibility of the DMA data
+// comes from each wave's own vmcnt wait before the barrier.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Raw buffer resource over `base` (uniform); offsets are 32-bit byte offsets.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
 }
 
-// One operand's slice (256 rows x 128 bytes) into LDS: 4 DMA instructions per
-// wave, each filling 8 LDS rows (1 KiB). HALF: only K chunks 0..3 exist (the
-// 64-byte tail of K), the other lanes stay idle.
-template <bool HALF>
-__device__ __forceinline__ void issue_slice(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds, const uint32_t (&off)[4],
-                                            int k0, int wid, int lane) {
+// One operand's slice (256 rows x 64 bytes) into LDS: kDmaPerWave DMA
+// instructions per wave, each filling 16 LDS rows (1 KiB).
+__device__ __forceinline__ void issue_slice(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds, const uint32_t (&off)[kDmaPerWave],
+                                            int k0, int wid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (HALF && ((lane & 7) ^ swz((wid * 4 + i) * 8 + (lane >> 3))) >= 4) continue;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wid * 4 + i) * 1024), 16, off[i], k0, 0, 0);
-  }
+  for (int i = 0; i < kDmaPerWave; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wid * kDmaPerWave + i) * 1024), 16, off[i], k0,
+                                             0, 0);
 }
 
 // Per wave: TI x TJ tiles of 16 x 16 (128 tokens x 64 channels).
 constexpr int TI = 8, TJ = 4;
 
-// NSUB 64-byte K steps out of one LDS slice into the accumulator tiles.
-template <int NSUB>
-__device__ __forceinline__ void mma_slice(const int8_t* la, const int8_t* lb, const int (&a_rd)[2],
-                                          const int (&b_rd)[2], v4i (&acc)[TI][TJ]) {
+// Fragments of one 64-byte K step: TI tiles of xq rows and TJ tiles of wq rows.
+struct Frags {
+  v4i a[TI], b[TJ];
+};
+
+__device__ __forceinline__ void read_frags(const int8_t* la, const int8_t* lb, int a_rd, int b_rd, Frags& f) {
 #pragma unroll
-  for (int ks = 0; ks < NSUB; ++ks) {
-    v4i a[TI], b[TJ];
+  for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const v4i*>(la + a_rd + i * 16 * kSlice);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) a[i] = *reinterpret_cast<const v4i*>(la + a_rd[ks] + i * 16 * kSlice);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) b[j] = *reinterpret_cast<const v4i*>(lb + b_rd[ks] + j * 16 * kSlice);
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[j], a[i], acc[i][j], 0, 0, 0);
-  }
+  for (int j = 0; j < TJ; ++j) f.b[j] = *reinterpret_cast<const v4i*>(lb + b_rd + j * 16 * kSlice);
 }
 
-template <int YDT, bool TAIL>
+// Scheduling of one step: each fragment read of the next slice goes out
+// between MFMAs of the current one (the MFMAs only need registers read a step
+// earlier), and nothing crosses the end of the step -- the compiler would
+// otherwise hoist the next step's MFMAs above the stage barrier, right behind
+// the reads they depend on.
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+#pragma unroll
+  for (int i = 0; i < TI + TJ; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - 2 * (TI + TJ), 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void mma(const Frags& f, v4i (&acc)[TI][TJ]) {
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+template <int YDT>
 __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                                       const int8_t* __restrict__ wq, const float* __restrict__ ws,
                                                       const float* __restrict__ bias, void* __restrict__ y,
                                                       int M, int N, int K, int tiles_m, int tiles_n, int group) {
-  // Two stages of both operands. Separate arrays let the compiler see that the
-  // DMA into one stage never aliases the fragment reads of the other, so it
-  // does not wait for the DMA before reading.
+  // Ring of kStages stages per operand, each its own array: the compiler then
+  // sees that a DMA into one stage never aliases the fragment reads of another
+  // and inserts no wait of its own before those reads.
   __shared__ __attribute__((aligned(1024))) int8_t lA0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) int8_t lB0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) int8_t lA1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lA2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lA3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) int8_t lB1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB3[kStageBytes];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS bases stay scalar
@@ -169,30 +197,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   map_tile(blockIdx.x, tiles_m * tiles_n, tiles_m, group, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;
 
-  // DMA lanes: instruction i of wave w fills LDS rows (w*4 + i)*8 .. +8 of one
-  // operand; lane -> row (lane / 8), 16-byte slot (lane % 8), which holds K
+  // DMA lanes: instruction i of wave w fills LDS rows (w*2 + i)*16 .. +16 of one
+  // operand; lane -> row (lane / 4), 16-byte slot (lane % 4), which holds K
   // chunk slot ^ swz(row). Rows past M or N re-read the last row (never stored).
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[kDmaPerWave], b_off[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wid * 4 + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int r = (wid * kDmaPerWave + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
     a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
     b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
   }
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
 
-  // Fragment reads: row R = base + 16 i + lane % 16, K chunk 4 ks + lane / 16.
+  // Fragment reads: row R = base + 16 i + lane % 16, K chunk lane / 16.
   const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
-  int a_rd[2], b_rd[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
-    const int c = 4 * ks + (lane >> 4);
-    a_rd[ks] = rra * kSlice + 16 * (c ^ swz(rra));
-    b_rd[ks] = rrb * kSlice + 16 * (c ^ swz(rrb));
-  }
+  const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
+  const int a_rd = rra * kSlice + 16 * ((lane >> 4) ^ swz(rra));
+  const int b_rd = rrb * kSlice + 16 * ((lane >> 4) ^ swz(rrb));
 
   v4i acc[TI][TJ];
 #pragma unroll
@@ -200,45 +223,56 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  // Full 128-byte slices ping-pong between the two stages. The loop body is one
-  // straight-line block (the accumulators then stay in AGPRs): each half waits
-  // for its stage, issues the next slice into the other stage -- clamped to the
-  // last slice, so the final issue is a harmless reload nobody reads -- and
-  // multiplies. An odd slice count leaves one slice in stage 0; TAIL adds the
-  // 64-byte remainder of K.
+  // Slices go round the 4-stage ring. At step k the fragments of slice k are
+  // already in registers (read during step k - 1); the step waits for slice
+  // k + 1 to land (vmcnt(8): each wave always has three slices, 4 DMA
+  // instructions each, in flight, since issue indices are clamped to the last
+  // slice and the final issues are harmless reloads), lets the barrier make it
+  // visible and free the stage slice k was read from, refills that stage with
+  // slice k + 4, reads the fragments of slice k + 1 and multiplies slice k
+  // meanwhile, so LDS latency hides behind the MFMAs. lgkmcnt(0) before the
+  // barrier: this wave's fragment reads of the stage about to be refilled are
+  // done.
   const int nk = K / kSlice;
-  const int last = nk > 0 ? (nk - 1) * kSlice : 0;
-  if (nk > 0) {
-    issue_slice<false>(ra, lA0, a_off, 0, wid, lane);
-    issue_slice<false>(rb, lB0, b_off, 0, wid, lane);
+  const int last = (nk - 1) * kSlice;
+  issue_slice(ra, lA0, a_off, 0, wid);
+  issue_slice(rb, lB0, b_off, 0, wid);
+  issue_slice(ra, lA1, a_off, min(kSlice, last), wid);
+  issue_slice(rb, lB1, b_off, min(kSlice, last), wid);
+  issue_slice(ra, lA2, a_off, min(2 * kSlice, last), wid);
+  issue_slice(rb, lB2, b_off, min(2 * kSlice, last), wid);
+  issue_slice(ra, lA3, a_off, min(3 * kSlice, last), wid);
+  issue_slice(rb, lB3, b_off, min(3 * kSlice, last), wid);
+  Frags f0, f1;
+  __builtin_amdgcn_s_waitcnt(0x0F7C);     // vmcnt(12): slice 0 landed
+  stage_barrier();
+  read_frags(lA0, lB0, a_rd, b_rd, f0);
+
+#define SQ_STEP(FC, FN, LA_NEXT, LB_NEXT, LA_FREE, LB_FREE)                 \
+  {                                                                     \
+    __builtin_amdgcn_s_waitcnt(0x0078); /* vmcnt(8) lgkmcnt(0) */       \
+    stage_barrier();                                                    \
+    const int kn = min((kt + 4) * kSlice, last);                        \
+    issue_slice(ra, LA_FREE, a_off, kn, wid);                           \
+    issue_slice(rb, LB_FREE, b_off, kn, wid);                           \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    read_frags(LA_NEXT, LB_NEXT, a_rd, b_rd, FN);                       \
+    mma(FC, acc);                                                       \
+    interleave_reads_with_mfma();                                       \
+    ++kt;                                                               \
   }
-  for (int kt = 0; kt + 1 < nk; kt += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA into stage 0 landed
-    __syncthreads();                      // ... every wave's; stage 1 is free again
-    issue_slice<false>(ra, lA1, a_off, (kt + 1) * kSlice, wid, lane);
-    issue_slice<false>(rb, lB1, b_off, (kt + 1) * kSlice, wid, lane);
-    mma_slice<2>(lA0, lB0, a_rd, b_rd, acc);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    const int k2 = min((kt + 2) * kSlice, last);
-    issue_slice<false>(ra, lA0, a_off, k2, wid, lane);
-    issue_slice<false>(rb, lB0, b_off, k2, wid, lane);
-    mma_slice<2>(lA1, lB1, a_rd, b_rd, acc);
+  int kt = 0;
+  for (; kt + 4 <= nk;) {
+    SQ_STEP(f0, f1, lA1, lB1, lA0, lB0)
+    SQ_STEP(f1, f0, lA2, lB2, lA1, lB1)
+    SQ_STEP(f0, f1, lA3, lB3, lA2, lB2)
+    SQ_STEP(f1, f0, lA0, lB0, lA3, lB3)
   }
-  if (nk & 1) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    mma_slice<2>(lA0, lB0, a_rd, b_rd, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);     // no DMA outstanding past this point
-  if constexpr (TAIL) {
-    __syncthreads();
-    issue_slice<true>(ra, lA1, a_off, nk * kSlice, wid, lane);
-    issue_slice<true>(rb, lB1, b_off, nk * kSlice, wid, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    mma_slice<1>(lA1, lB1, a_rd, b_rd, acc);
-  }
+  if (kt < nk) SQ_STEP(f0, f1, lA1, lB1, lA0, lB0)
+  if (kt < nk) SQ_STEP(f1, f0, lA2, lB2, lA1, lB1)
+  if (kt < nk) SQ_STEP(f0, f1, lA3, lB3, lA2, lB2)
+#undef SQ_STEP
+  __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): no DMA into LDS outlives the loop
 
   // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
 #pragma unroll
@@ -336,12 +370,8 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
-  if (g.K % kSlice)
-    hipLaunchKernelGGL((k_gemm_tile<YDT, true>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
-                       g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
-  else
-    hipLaunchKernelGGL((k_gemm_tile<YDT, false>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale,
-                       g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  hipLaunchKernelGGL((k_gemm_tile<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
+                     g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
   return hipGetLastError();
 }
 
