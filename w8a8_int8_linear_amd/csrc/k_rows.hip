@@ -1,89 +1,103 @@
 // Row-streaming kernels: fused norm + per-token INT8 quantisation, calibration
-// absmax, and the three steps of the offline fold (weight column maxima,
-// smoothing factors, per-output-channel weight quantisation).
+// absmax, and the offline fold (weight column maxima, smoothing factors; the
+// weight codes are the NONE-norm quantiser run over W with gamma = s).
 //
-// One workgroup owns one row (or a few rows for calibration); the row stays in
-// registers between the statistics, the normalisation and the quantisation, so
-// each element is read from HBM once and its code written once.
+// The quantiser keeps a whole row in registers between its statistics, its
+// normalisation and its codes, so each element is read from HBM once and its
+// code written once. Workgroups stride over rows and load the next row while
+// they work on the current one, which hides HBM latency even when only one
+// workgroup fits on a CU (a 20480-wide binary32 row is 80 KiB of registers).
 #include "sq_device.h"
 #include "sq_launch.h"
 #include "smoothquant.h"
 
 namespace sq {
 
-// Load one row (K elements, K % 64 == 0) into registers and apply the norm.
-// On return v holds y as binary32: LayerNorm ((x - mean) * rstd) * gamma + beta,
-// RMSNorm (x * rstd) * gamma, or x * gamma; a NULL gamma/beta means 1/0. The
-// statistics are summed in binary64 in a fixed order and rounded once to
-// binary32; rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
-template <typename T, int NORM, int NV, int THREADS>
-__device__ __forceinline__ void row_y(const char* __restrict__ xrow, int K, const float* __restrict__ gamma,
-                                      const float* __restrict__ beta, float eps, float (&v)[NV][8],
-                                      double* red) {
-  constexpr int B = Storage<T>::kBytes;
-  const int nvec = K >> 3;
+// A row held as raw 16-byte vectors: thread t owns vectors t, t + THREADS, ...
+template <typename T, int NV, int THREADS>
+struct RawRow {
+  Raw8<T> r[NV];
+  __device__ __forceinline__ void load(const void* x, int64_t row, int K) {
+    const char* xrow = static_cast<const char*>(x) + row * K * Storage<T>::kBytes;
+    const int nvec = K >> 3;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int vi = threadIdx.x + i * THREADS;
-    if (vi < nvec) {
-      load8<T>(xrow + static_cast<size_t>(vi) * 8 * B, v[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+    for (int i = 0; i < NV; ++i) {
+      const int vi = threadIdx.x + i * THREADS;
+      if (vi < nvec) raw_load<T>(xrow + static_cast<size_t>(vi) * 8 * Storage<T>::kBytes, r[i]);
     }
   }
+};
+
+// Statistics of a binary32 row held in registers (padding holds zeros) and the
+// normalised y in place: LayerNorm ((x - mean) * rstd) * gamma + beta, RMSNorm
+// (x * rstd) * gamma; a NULL gamma / beta means 1 / 0. Sums are taken in
+// binary64 in a fixed order (LayerNorm: two passes, centred on the binary64
+// mean) and rounded once to binary32; rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
+template <int NORM, int NV, int THREADS>
+__device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const float* __restrict__ gamma,
+                                              const float* __restrict__ beta, float eps, double* red) {
+  const int nvec = K >> 3;
   float mu = 0.0f, r = 1.0f;
   if constexpr (NORM == SQ_NORM_LAYERNORM) {
+    // one partial sum per vector (independent dependency chains), combined in a fixed order
+    double p1[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      p1[i] = 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p1[i] += static_cast<double>(v[i][e]);
+    }
     double s1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s1 += p1[i];
+    s1 = block_sum<THREADS>(s1, red);
+    const double mean = s1 / static_cast<double>(K);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s1 += static_cast<double>(v[i][e]);   // padding holds zeros
-    s1 = block_sum<THREADS>(s1, red);
-    const double mean = s1 / static_cast<double>(K);
-    double s2 = 0.0;
+      for (int e = 0; e < 8; ++e) opaque(v[i][e]);   // convert again below rather than keep 2*8*NV doubles
+    double p2[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+      p2[i] = 0.0;
       if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const double d = static_cast<double>(v[i][e]) - mean;
-          s2 = __builtin_fma(d, d, s2);
+          p2[i] = __builtin_fma(d, d, p2[i]);
         }
       }
     }
-    s2 = block_sum<THREADS>(s2, red);
-    mu = static_cast<float>(mean);
-    const float var = static_cast<float>(s2 / static_cast<double>(K));
-    r = div_rn(1.0f, sqrt_rn(add_rn(var, eps)));
-  } else if constexpr (NORM == SQ_NORM_RMSNORM) {
     double s2 = 0.0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NV; ++i) s2 += p2[i];
+    s2 = block_sum<THREADS>(s2, red);
+    mu = static_cast<float>(mean);
+    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
+  } else if constexpr (NORM == SQ_NORM_RMSNORM) {
+    double p2[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      p2[i] = 0.0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const double d = static_cast<double>(v[i][e]);
-        s2 = __builtin_fma(d, d, s2);
+        p2[i] = __builtin_fma(d, d, p2[i]);
       }
+    }
+    double s2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s2 += p2[i];
     s2 = block_sum<THREADS>(s2, red);
-    const float var = static_cast<float>(s2 / static_cast<double>(K));
-    r = div_rn(1.0f, sqrt_rn(add_rn(var, eps)));
+    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = threadIdx.x + i * THREADS;
     if (vi >= nvec) continue;
     float g[8], b[8];
-    if (gamma) {
-      const float4 g0 = reinterpret_cast<const float4*>(gamma)[2 * vi];
-      const float4 g1 = reinterpret_cast<const float4*>(gamma)[2 * vi + 1];
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-    }
-    if (NORM == SQ_NORM_LAYERNORM && beta) {
-      const float4 b0 = reinterpret_cast<const float4*>(beta)[2 * vi];
-      const float4 b1 = reinterpret_cast<const float4*>(beta)[2 * vi + 1];
-      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
-    }
+    if (gamma) load8_f32(gamma + 8 * vi, g);
+    if (NORM == SQ_NORM_LAYERNORM && beta) load8_f32(beta + 8 * vi, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float t = v[i][e];
@@ -96,61 +110,165 @@ __device__ __forceinline__ void row_y(const char* __restrict__ xrow, int K, cons
   }
 }
 
-// Fused norm + per-token quantisation: one workgroup per row.
+// y of vector i of a raw row for the NONE norm: x, or fl32(x * gamma).
+template <typename T, int NV, int THREADS>
+__device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i, const float* __restrict__ gamma,
+                                       float y[8]) {
+  widen8<T>(raw.r[i], y);
+  if (gamma) {
+    float g[8];
+    load8_f32(gamma + 8 * (threadIdx.x + i * THREADS), g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = mul_rn(y[e], g[e]);
+  }
+}
+
+// Quantise one row held raw in registers, write its codes and step, and refill
+// the raw buffer with row `next` (if next < M) as soon as each part of it is
+// free, so the next row's loads overlap this row's work within one buffer.
+//  NONE: two passes over the raw row (the max of |x * gamma|, then the codes),
+//        recomputing the product instead of holding binary32 copies; vector i
+//        is refilled right after its codes are written.
+//  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
+//        normalise in place, then max and codes.
 template <typename T, int NORM, int NV, int THREADS>
-__global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__ x, int K,
+__device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x, int64_t row,
+                                             int64_t next, int M, int K, const float* __restrict__ gamma,
+                                             const float* __restrict__ beta, float eps, int8_t* __restrict__ xq,
+                                             float* __restrict__ x_scale, double* red) {
+  const int nvec = K >> 3;
+  constexpr int B = Storage<T>::kBytes;
+  int8_t* qrow = xq + row * K;
+  const bool refill = next < M;
+  // Address of the next row, formed unconditionally and used only when
+  // refill holds. (Written as refill ? next : row, ROCm 7.2's compiler turns
+  // the select into an s_cselect on a stale SCC -- the 64-bit compare went to
+  // VCC -- and reloads the current row.)
+  const char* nrow = static_cast<const char*>(x) + next * K * B;
+  if constexpr (NORM == SQ_NORM_NONE) {
+    float pm[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      pm[i] = 0.0f;
+      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
+        float y[8];
+        none_y<T, NV, THREADS>(raw, i, gamma, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pm[i] = fmaxf(pm[i], fabsf(y[e]));
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
+    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red));
+    const float step = int8_step(amax);
+    if (threadIdx.x == 0) x_scale[row] = step;
+    const Quantizer qz(step);
+    // recompute x * gamma below rather than keep pass one's 8*NV products (or gamma) in registers
+#pragma unroll
+    for (int i = 0; i < NV; ++i) opaque(raw.r[i].a);
+    memory_opaque();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = threadIdx.x + i * THREADS;
+      if (vi < nvec) {
+        float y[8];
+        none_y<T, NV, THREADS>(raw, i, gamma, y);
+        *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(y);
+        if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+      }
+    }
+  } else {
+    float v[NV][8];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
+        widen8<T>(raw.r[i], v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+      }
+    }
+    if (refill) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int vi = threadIdx.x + i * THREADS;
+        if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+      }
+    }
+    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red);
+    float pm[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      pm[i] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pm[i] = fmaxf(pm[i], fabsf(v[i][e]));
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
+    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red));
+    const float step = int8_step(amax);
+    if (threadIdx.x == 0) x_scale[row] = step;
+    const Quantizer qz(step);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = threadIdx.x + i * THREADS;
+      if (vi < nvec) *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(v[i]);
+    }
+  }
+}
+
+// Fused norm + per-token quantisation. Workgroup b handles rows b, b + G, ...
+// (G = gridDim.x <= M); one raw row buffer, refilled with the next row while
+// the current one is being processed.
+template <typename T, int NORM, int NV, int THREADS>
+__global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__ x, int M, int K,
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, float eps,
                                                         int8_t* __restrict__ xq, float* __restrict__ x_scale) {
   __shared__ double red[THREADS / kWave];
-  const int64_t row = blockIdx.x;
-  const char* xrow = static_cast<const char*>(x) + row * K * Storage<T>::kBytes;
-  float v[NV][8];
-  row_y<T, NORM, NV, THREADS>(xrow, K, gamma, beta, eps, v, red);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
-  amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red));
-  const float step = int8_step(amax);
-  if (threadIdx.x == 0) x_scale[row] = step;
-  const Quantizer qz(step);
-  int8_t* qrow = xq + row * K;
-  const int nvec = K >> 3;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int vi = threadIdx.x + i * THREADS;
-    if (vi < nvec) *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(v[i]);
-  }
+  const int64_t G = gridDim.x;
+  RawRow<T, NV, THREADS> raw;
+  raw.load(x, blockIdx.x, K);
+  for (int64_t row = blockIdx.x; row < M; row += G)
+    quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, beta, eps, xq, x_scale, red);
 }
 
-// Calibration: each workgroup normalises `rows` consecutive rows, keeps the
-// per-column max of |y| in registers and merges it into absmax with an
-// order-free atomic max.
+// Calibration with a norm: workgroups stride over rows, normalise each with the
+// unfolded gamma / beta, keep the per-column max of |y| in registers and merge
+// it into absmax with an order-free atomic max at the end.
 template <typename T, int NORM, int NV, int THREADS>
-__global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ x, int M, int K, int rows,
+__global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ x, int M, int K,
                                                        const float* __restrict__ gamma,
                                                        const float* __restrict__ beta, float eps,
                                                        float* __restrict__ absmax) {
   __shared__ double red[THREADS / kWave];
+  const int nvec = K >> 3;
   float cm[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) cm[i][e] = 0.0f;
-  const int r0 = blockIdx.x * rows;
-  const int r1 = min(M, r0 + rows);
-  for (int r = r0; r < r1; ++r) {
-    const char* xrow = static_cast<const char*>(x) + static_cast<int64_t>(r) * K * Storage<T>::kBytes;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    RawRow<T, NV, THREADS> raw;
+    raw.load(x, row, K);
     float v[NV][8];
-    row_y<T, NORM, NV, THREADS>(xrow, K, gamma, beta, eps, v, red);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
+        widen8<T>(raw.r[i], v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+      }
+    }
+    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) cm[i][e] = fmaxf(cm[i][e], fabsf(v[i][e]));
   }
-  const int nvec = K >> 3;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = threadIdx.x + i * THREADS;
@@ -160,23 +278,25 @@ __global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ 
   }
 }
 
-// Fold step 1: colmax[j] = max_n |W[n, j]| (colmax pre-zeroed). Each thread owns
-// 8 adjacent columns and walks `rows` rows; the column maxima merge by atomic max.
+// Column maxima colmax[j] = max(colmax[j], max_n |X[n, j]|): the weight column
+// maxima of the fold (colmax pre-zeroed), and calibration without a norm (the
+// running absmax). Each thread owns 8 adjacent columns and walks `rows` rows;
+// the maxima merge by atomic max.
 template <typename T>
 __global__ __launch_bounds__(256) void k_colmax(const void* __restrict__ w, int N, int K, int rows,
                                                 float* __restrict__ colmax) {
   const int vi = blockIdx.x * 256 + threadIdx.x;
   if (vi >= (K >> 3)) return;
-  const int r0 = blockIdx.y * rows;
-  const int r1 = min(N, r0 + rows);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows;
+  const int64_t r1 = r0 + rows < N ? r0 + rows : N;
   constexpr int B = Storage<T>::kBytes;
   const char* base = static_cast<const char*>(w) + static_cast<size_t>(vi) * 8 * B;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int r = r0;
+  int64_t r = r0;
   for (; r + 4 <= r1; r += 4) {
     float v[4][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load8<T>(base + static_cast<int64_t>(r + u) * K * B, v[u]);
+    for (int u = 0; u < 4; ++u) load8<T>(base + (r + u) * K * B, v[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -184,7 +304,7 @@ __global__ __launch_bounds__(256) void k_colmax(const void* __restrict__ w, int 
   }
   for (; r < r1; ++r) {
     float v[8];
-    load8<T>(base + static_cast<int64_t>(r) * K * B, v);
+    load8<T>(base + r * K * B, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(v[e]));
   }
@@ -197,7 +317,7 @@ __global__ void k_fill_zero(float* __restrict__ p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// Fold step 2: s_j = max(fl32(max(a_j, eps)^alpha / max(w_j, eps)^(1 - alpha)), eps)
+// Smoothing factors: s_j = max(fl32(max(a_j, eps)^alpha / max(w_j, eps)^(1 - alpha)), eps)
 // with the quotient in binary64; gamma' = gamma / s (1 / s without gamma),
 // beta' = beta / s. s_io holds the column maxima on entry and s on exit.
 __global__ void k_scales(const float* __restrict__ act_absmax, float* __restrict__ s_io, int K, double alpha,
@@ -220,8 +340,7 @@ namespace {
 
 struct RowCfg { int threads, nv; };
 
-// Smallest (threads, vectors per thread) covering K/8 vectors, keeping at most
-// ~80 binary32 values per thread in registers.
+// Smallest (threads, vectors per thread) covering K/8 vectors of the row.
 RowCfg row_cfg(int K) {
   const int nvec = K >> 3;
   static const RowCfg table[] = {{256, 1}, {256, 2}, {256, 3}, {256, 4}, {512, 3},  {512, 4},   {512, 5},
@@ -231,25 +350,67 @@ RowCfg row_cfg(int K) {
   return {1024, 17};
 }
 
+// Workgroups that fit on the device at once (all CUs x the kernel's occupancy).
+hipError_t resident_blocks(const void* kernel, int threads, int* out) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+  *out = (e == hipSuccess) ? cus * (per_cu > 0 ? per_cu : 1) : 0;
+  return e;
+}
+
 template <typename T, int NORM, int NV, int THREADS>
 hipError_t launch_nq(const RowArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_norm_quant<T, NORM, NV, THREADS>), dim3(a.rows), dim3(THREADS), 0, st, a.x, a.K,
-                     a.gamma, a.beta, a.eps, a.xq, a.x_scale);
+  auto kern = k_norm_quant<T, NORM, NV, THREADS>;
+  int cap = 0;
+  if (hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), THREADS, &cap)) return e;
+  const int grid = static_cast<int>(a.rows < cap ? a.rows : cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, st, a.x, static_cast<int>(a.rows), a.K, a.gamma, a.beta,
+                     a.eps, a.xq, a.x_scale);
   return hipGetLastError();
 }
 
 template <typename T, int NORM, int NV, int THREADS>
 hipError_t launch_cal(const RowArgs& a, hipStream_t st) {
-  const int per = 4;
-  const int blocks = static_cast<int>((a.rows + per - 1) / per);
-  hipLaunchKernelGGL((k_calibrate<T, NORM, NV, THREADS>), dim3(blocks), dim3(THREADS), 0, st, a.x,
-                     static_cast<int>(a.rows), a.K, per, a.gamma, a.beta, a.eps, a.absmax);
+  // enough rows per workgroup to keep the atomic merges few, enough workgroups to fill the device
+  auto kern = k_calibrate<T, NORM, NV, THREADS>;
+  int cap = 0;
+  if (hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), THREADS, &cap)) return e;
+  int64_t grid = (a.rows + 3) / 4;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(kern, dim3(static_cast<int>(grid)), dim3(THREADS), 0, st, a.x, static_cast<int>(a.rows), a.K,
+                     a.gamma, a.beta, a.eps, a.absmax);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_colmax(const void* x, int64_t N, int K, float* colmax, hipStream_t st) {
+  // rows per workgroup: ~2048 workgroups in all (each merges 8 columns per thread
+  // by atomic max, so fewer, longer workgroups keep the atomics few), >= 16 rows,
+  // and gridDim.y within 65535
+  const int64_t col_blocks = ((K >> 3) + 255) / 256;
+  int64_t rows = (N * col_blocks + 2047) / 2048;
+  rows = rows < 16 ? 16 : (rows + 3) / 4 * 4;
+  while ((N + rows - 1) / rows > 65535) rows *= 2;
+  const dim3 grid(((K >> 3) + 255) / 256, static_cast<unsigned>((N + rows - 1) / rows));
+  hipLaunchKernelGGL(k_colmax<T>, grid, dim3(256), 0, st, x, static_cast<int>(N), K, static_cast<int>(rows), colmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_colmax_dt(sq_dtype dt, const void* x, int64_t N, int K, float* colmax, hipStream_t st) {
+  switch (dt) {
+    case SQ_DT_F32: return launch_colmax<f32_t>(x, N, K, colmax, st);
+    case SQ_DT_F16: return launch_colmax<f16_t>(x, N, K, colmax, st);
+    case SQ_DT_BF16: return launch_colmax<bf16_t>(x, N, K, colmax, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool CAL, typename T, int NORM, int NV, int THREADS>
 hipError_t dispatch_one(const RowArgs& a, hipStream_t st) {
-  return CAL ? launch_cal<T, NORM, NV, THREADS>(a, st) : launch_nq<T, NORM, NV, THREADS>(a, st);
+  if constexpr (CAL) return launch_cal<T, NORM, NV, THREADS>(a, st);
+  else return launch_nq<T, NORM, NV, THREADS>(a, st);
 }
 
 template <bool CAL, typename T, int NORM>
@@ -268,7 +429,9 @@ hipError_t dispatch_cfg(const RowArgs& a, hipStream_t st) {
 template <bool CAL, typename T>
 hipError_t dispatch_norm(const RowArgs& a, hipStream_t st) {
   switch (a.norm) {
-    case SQ_NORM_NONE: return dispatch_cfg<CAL, T, SQ_NORM_NONE>(a, st);
+    case SQ_NORM_NONE:
+      if constexpr (CAL) return hipErrorInvalidValue;   // NONE calibration is a column max
+      else return dispatch_cfg<CAL, T, SQ_NORM_NONE>(a, st);
     case SQ_NORM_LAYERNORM: return dispatch_cfg<CAL, T, SQ_NORM_LAYERNORM>(a, st);
     case SQ_NORM_RMSNORM: return dispatch_cfg<CAL, T, SQ_NORM_RMSNORM>(a, st);
   }
@@ -289,25 +452,18 @@ hipError_t dispatch_dtype(const RowArgs& a, hipStream_t st) {
 
 hipError_t launch_norm_quant(const RowArgs& a, hipStream_t st) { return dispatch_dtype<false>(a, st); }
 
-hipError_t launch_calibrate(const RowArgs& a, hipStream_t st) { return dispatch_dtype<true>(a, st); }
+hipError_t launch_calibrate(const RowArgs& a, hipStream_t st) {
+  // Without a norm the linear's input is x itself: the running absmax is a column max.
+  if (a.norm == SQ_NORM_NONE) return launch_colmax_dt(a.dtype, a.x, a.rows, a.K, a.absmax, st);
+  return dispatch_dtype<true>(a, st);
+}
 
 hipError_t launch_fold_colmax_scales(const FoldArgs& f, hipStream_t st) {
   const int K = static_cast<int>(f.K);
   hipLaunchKernelGGL(k_fill_zero, dim3((K + 255) / 256), dim3(256), 0, st, f.s_out, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int rows = 256;                                   // keep gridDim.y within 65535
-  while ((f.N + rows - 1) / rows > 65535) rows *= 2;
-  const dim3 grid(((K >> 3) + 255) / 256, static_cast<unsigned>((f.N + rows - 1) / rows));
-  const int N = static_cast<int>(f.N);
-  switch (f.dtype) {
-    case SQ_DT_F32: hipLaunchKernelGGL(k_colmax<f32_t>, grid, dim3(256), 0, st, f.w, N, K, rows, f.s_out); break;
-    case SQ_DT_F16: hipLaunchKernelGGL(k_colmax<f16_t>, grid, dim3(256), 0, st, f.w, N, K, rows, f.s_out); break;
-    case SQ_DT_BF16: hipLaunchKernelGGL(k_colmax<bf16_t>, grid, dim3(256), 0, st, f.w, N, K, rows, f.s_out); break;
-    default: return hipErrorInvalidValue;
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = launch_colmax_dt(f.dtype, f.w, f.N, K, f.s_out, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_scales, dim3((K + 255) / 256), dim3(256), 0, st, f.act_absmax, f.s_out, K, f.alpha,
                      f.eps, f.gamma, f.beta, f.gamma_out, f.beta_out);
   return hipGetLastError();

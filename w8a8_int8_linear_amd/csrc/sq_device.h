@@ -25,6 +25,14 @@ __device__ __forceinline__ float mul_rn(float a, float b) { return a * b; }
 __device__ __forceinline__ float div_rn(float a, float b) { return a / b; }
 __device__ __forceinline__ float sqrt_rn(float a) { return __builtin_sqrtf(a); }
 
+// Make a register value opaque to the optimiser (no instruction emitted): a
+// later pass over the same data then recomputes what it needs instead of the
+// compiler keeping an earlier pass's intermediates alive, which would blow
+// the register budget of a row held in registers.
+__device__ __forceinline__ void opaque(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+__device__ __forceinline__ void memory_opaque() { asm volatile("" ::: "memory"); }
+
 // ----------------------------------------------------------------------------- storage types
 struct f32_t {};
 struct f16_t {};
@@ -41,19 +49,29 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }
 
-// Load 8 consecutive elements (p is 16-byte aligned) and widen them exactly to binary32.
-template <typename T> __device__ __forceinline__ void load8(const void* p, float v[8]);
+// Raw storage of 8 consecutive elements (one 16-byte load; two for binary32).
+template <typename T> struct Raw8 { uint4 a; };
+template <> struct Raw8<f32_t> { uint4 a, b; };
 
-template <> __device__ __forceinline__ void load8<f32_t>(const void* p, float v[8]) {
-  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
-  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+template <typename T> __device__ __forceinline__ void raw_load(const void* p, Raw8<T>& r) {
+  r.a = *reinterpret_cast<const uint4*>(p);
+}
+template <> __device__ __forceinline__ void raw_load<f32_t>(const void* p, Raw8<f32_t>& r) {
+  r.a = reinterpret_cast<const uint4*>(p)[0];
+  r.b = reinterpret_cast<const uint4*>(p)[1];
 }
 
-template <> __device__ __forceinline__ void load8<f16_t>(const void* p, float v[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+// Widen 8 stored elements exactly to binary32.
+template <typename T> __device__ __forceinline__ void widen8(const Raw8<T>& r, float v[8]);
+
+template <> __device__ __forceinline__ void widen8<f32_t>(const Raw8<f32_t>& r, float v[8]) {
+  v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y); v[2] = __uint_as_float(r.a.z);
+  v[3] = __uint_as_float(r.a.w); v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+  v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+}
+
+template <> __device__ __forceinline__ void widen8<f16_t>(const Raw8<f16_t>& r, float v[8]) {
+  const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = f16_bits_to_f32(w[i] & 0xffffu);
@@ -61,14 +79,27 @@ template <> __device__ __forceinline__ void load8<f16_t>(const void* p, float v[
   }
 }
 
-template <> __device__ __forceinline__ void load8<bf16_t>(const void* p, float v[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+template <> __device__ __forceinline__ void widen8<bf16_t>(const Raw8<bf16_t>& r, float v[8]) {
+  const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = __uint_as_float(w[i] << 16);
     v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
+}
+
+// Load 8 consecutive elements (p is 16-byte aligned) and widen them exactly to binary32.
+template <typename T> __device__ __forceinline__ void load8(const void* p, float v[8]) {
+  Raw8<T> r;
+  raw_load<T>(p, r);
+  widen8<T>(r, v);
+}
+
+// 8 binary32 values from a 16-byte-aligned fp32 vector (gamma, beta, s).
+__device__ __forceinline__ void load8_f32(const float* p, float v[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 // ----------------------------------------------------------------------------- output conversion
@@ -145,7 +176,9 @@ struct Quantizer {
     exact_only = st < 0x1p-100f;
     rcp = zero ? 0.0f : div_rn(1.0f, st);
   }
-  // Codes of 8 values, packed little-endian into two 32-bit words.
+  // Codes of 8 values, packed little-endian into two 32-bit words. On the
+  // fast path |t| <= amax * fl32(1/step) < 127.5, so rne(t) needs no clamp;
+  // the exact path clamps (a subnormal step may push the quotient past 127).
   __device__ __forceinline__ uint2 codes8(const float y[8]) const {
     float q[8];
     bool slow = exact_only;
@@ -157,13 +190,12 @@ struct Quantizer {
     }
     if (slow) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = rintf(div_rn(y[i], step));
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(rintf(div_rn(y[i], step)), -127.0f), 127.0f);
     }
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = zero ? 0 : static_cast<int>(fminf(fmaxf(q[i], -127.0f), 127.0f));
-      const uint32_t b = static_cast<uint32_t>(c) & 0xffu;
+      const uint32_t b = static_cast<uint32_t>(zero ? 0 : static_cast<int>(q[i])) & 0xffu;
       if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
     }
     return make_uint2(w0, w1);
