@@ -40,7 +40,114 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration runs)")
+    p.add_argument("--summarize-counters", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="turn rocprofv3 CSV output of this benchmark into profiles/ summaries and exit")
     return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- counter summaries
+
+GEMM_SOURCES = ["w8a8_int8_linear_amd/csrc/k_gemm.hip", "w8a8_int8_linear_amd/csrc/sq_device.h",
+                "w8a8_int8_linear_amd/build.py"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "k_gemm_tile_traffic.json")
+
+
+def gemm_source_hash() -> str:
+    """Hash of everything that shapes the GEMM kernel's code (sources and build flags)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None when the
+    kernel has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec
+
+
+def summarize_counters(trace_dir, fetch_dir, write_dir):
+    """rocprofv3 CSVs of `bench.py` runs -> profiles/*.md and the GEMM traffic record.
+
+    FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what it reads for
+    the plain device copy of --copy-probe-mib MiB that the counter runs add at the end.
+    """
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def one(d, pat):
+        hits = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        if not hits:
+            raise SystemExit(f"no {pat} under {d}")
+        return hits[0]
+
+    stats = list(csv.DictReader(open(one(trace_dir, "*kernel_stats.csv"))))
+    counters = {}
+    for name, d in [("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)]:
+        rows = [r for r in csv.DictReader(open(one(d, "*counter_collection.csv"))) if r["Counter_Name"] == name]
+        copy = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        copy = max(copy, key=lambda r: float(r["Counter_Value"]))
+        per = defaultdict(list)
+        for r in rows:
+            if "sq::" in r["Kernel_Name"]:
+                per[(int(r["Dispatch_Id"]), r["Kernel_Name"])] = float(r["Counter_Value"])
+        counters[name] = {"copy_kib": float(copy["Counter_Value"]), "per": per}
+    copy_kib = 1024.0 * max(1, int(os.environ.get("COPY_PROBE_MIB", "1024")))
+    scale = {k: copy_kib / v["copy_kib"] for k, v in counters.items()}
+    gemm = sorted(k for k in counters["FETCH_SIZE"]["per"] if "k_gemm" in k[1])
+    gemm_w = sorted(k for k in counters["WRITE_SIZE"]["per"] if "k_gemm" in k[1])
+    launches = []
+    for (fd, _), (wd, _) in zip(gemm, gemm_w):
+        fb = counters["FETCH_SIZE"]["per"][(fd, _)] * scale["FETCH_SIZE"] * 1024
+        wb = counters["WRITE_SIZE"]["per"][(wd, _)] * scale["WRITE_SIZE"] * 1024
+        launches.append({"fetch_bytes": fb, "write_bytes": wb})
+    cmd_trace = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+                 "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline")
+    cmd_pmc = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o run --output-format csv -- "
+               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-probe-mib 1024")
+    rec = {"kernel": "k_gemm_tile", "workload": "mtnlg530b_width_m8192_h20480 (fc1 then fc2)",
+           "source_sha256": gemm_source_hash(), "fetch_scale": scale["FETCH_SIZE"],
+           "write_scale": scale["WRITE_SIZE"], "launches": launches,
+           "traffic_bytes_per_launch": sum(l["fetch_bytes"] + l["write_bytes"] for l in launches) / len(launches),
+           "commands": [cmd_trace, cmd_pmc]}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# rocprofv3 kernel statistics: bench.py, MT-NLG-530B-width layer (M=8192, hidden 20480)", "",
+             f"Command: `{cmd_trace}`", "",
+             "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "sq::" in r["Name"]:
+            short = r["Name"].split("(")[0].replace("void ", "")
+            lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                         f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} |")
+    lines += ["", "Each step launches every kernel of both sites (fc1 behind LayerNorm, fc2 without a norm); "
+              "k_gemm_tile's average covers both GEMM shapes (8192x81920x20480 and 8192x20480x81920)."]
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_mtnlg530b_width.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE, WRITE_SIZE): MT-NLG-530B-width layer", "",
+             f"Commands: `{cmd_pmc}` (one run per counter).", "",
+             f"Scale: the 1 GiB device copy reads FETCH_SIZE = {counters['FETCH_SIZE']['copy_kib']:.0f} KiB "
+             f"and WRITE_SIZE = {counters['WRITE_SIZE']['copy_kib']:.0f} KiB, so FETCH_SIZE is multiplied by "
+             f"{scale['FETCH_SIZE']:.3f} and WRITE_SIZE by {scale['WRITE_SIZE']:.3f}.", "",
+             "| dispatch | kernel | fetched GB | written GB |", "|---|---|---|---|"]
+    for (fd, name), (wd, _) in zip(sorted(counters["FETCH_SIZE"]["per"]), sorted(counters["WRITE_SIZE"]["per"])):
+        fb = counters["FETCH_SIZE"]["per"][(fd, name)] * scale["FETCH_SIZE"] * 1024 / 1e9
+        wb = counters["WRITE_SIZE"]["per"][(wd, name)] * scale["WRITE_SIZE"] * 1024 / 1e9
+        lines.append(f"| {fd} | `{name.split('(')[0].replace('void ', '')}` | {fb:.3f} | {wb:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_mtnlg530b_width.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(rec, indent=1))
 
 
 class Timer:
@@ -165,6 +272,9 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",
                           "n_gpus": args.gpus}))
@@ -203,6 +313,10 @@ def main():
     g_ms = [rep[f"gemm{i}"]["ms"] for i in range(len(sites))]
     g_ops = [2.0 * d["m"] * d["n"] * d["k"] for d in sites]
     achieved = sum(g_ops) / (sum(g_ms) * 1e-3) / 1e12
+    osize = {"f32": 4, "f16": 2, "bf16": 2}[wl.out_dtype]
+    alg_bytes = [d["n"] * d["k"] + 4 * d["n"] + d["m"] * d["k"] + 4 * d["m"] + osize * d["m"] * d["n"] for d in sites]
+    rec = recorded_traffic() if args.workload == 5 and m == 8192 else None
+    traffic = rec["traffic_bytes_per_launch"] if rec else None
     out = {
         "metric": "W8A8 GEMM TOPS + % INT8 MFMA peak; norm+quant kernel HBM GB/s",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -213,7 +327,9 @@ def main():
                    "alpha": wl.alpha, "act_dtype": wl.dtype, "out_dtype": wl.out_dtype, "m_cal": wl.m_cal},
         "roofline": {"bound": "mfma", "kernel": "k_gemm_tile", "achieved": round(achieved, 1),
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic, "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes_per_launch": sum(alg_bytes) / len(alg_bytes),
+                     "ops_per_launch": sum(g_ops) / len(g_ops)},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in rep.items()},
         "hbm_peak_GBps": PEAK_HBM_GBS,
