@@ -139,7 +139,10 @@ def test_fold(dtype, norm, alpha, nk):
 
 GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 1024), (65, 64, 64),
                (256, 256, 128), (300, 520, 192), (513, 257, 640), (1000, 1000, 1088), (2, 9216, 9216),
-               (600, 700, 4096)]
+               (600, 700, 4096),
+               # decode kernel: every token-tile count, K tails of 64 / 128 / 192 bytes past a 256-byte segment
+               (16, 48, 320), (32, 100, 576), (33, 17, 192), (48, 70, 4160), (63, 130, 2112), (64, 2048, 9216),
+               (5, 36, 1984)]
 
 
 @pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))

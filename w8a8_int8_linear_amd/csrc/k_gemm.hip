@@ -12,10 +12,8 @@
 //    16-byte chunks so the fragment reads are bank-conflict free. Workgroups are
 //    mapped to tiles XCD by XCD and in column groups, so tiles that share
 //    operand rows run at the same time on the same L2.
-//  * k_gemm_skinny -- decode shapes (M <= 64), bound by streaming wq from HBM.
-//    A workgroup owns 16 output channels; its four waves split K, each streams
-//    its 16 rows of wq straight into MFMA operands and the partial accumulators
-//    are summed through LDS.
+//  * k_gemm_skinny -- decode shapes (M <= 64), bound by streaming wq from HBM
+//    (described at the kernel).
 //
 // MFMA operand order: the A operand (rows = lane % 16) carries 16 rows of wq and
 // the B operand (columns = lane % 16) 16 rows of xq, so the 16x16 result tile
@@ -26,6 +24,8 @@
 #include "sq_device.h"
 #include "sq_launch.h"
 #include "smoothquant.h"
+
+#include <type_traits>
 
 namespace sq {
 
@@ -235,12 +235,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   // done.
   const int nk = K / kSlice;
   const int last = (nk - 1) * kSlice;
+  // in slice order: the waits below count DMAs in issue order, and the stages
+  // being distinct objects the compiler could otherwise interleave them
   issue_slice(ra, lA0, a_off, 0, wid);
   issue_slice(rb, lB0, b_off, 0, wid);
+  memory_opaque();
   issue_slice(ra, lA1, a_off, min(kSlice, last), wid);
   issue_slice(rb, lB1, b_off, min(kSlice, last), wid);
+  memory_opaque();
   issue_slice(ra, lA2, a_off, min(2 * kSlice, last), wid);
   issue_slice(rb, lB2, b_off, min(2 * kSlice, last), wid);
+  memory_opaque();
   issue_slice(ra, lA3, a_off, min(3 * kSlice, last), wid);
   issue_slice(rb, lB3, b_off, min(3 * kSlice, last), wid);
   Frags f0, f1;
@@ -290,82 +295,252 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
 
 // ----------------------------------------------------------------------------- skinny kernel
 
-template <int MT, int YDT>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const int8_t* __restrict__ xq, const float* __restrict__ xs,
-                                                     const int8_t* __restrict__ wq, const float* __restrict__ ws,
-                                                     const float* __restrict__ bias, void* __restrict__ y,
-                                                     int M, int N, int K) {
-  __shared__ v4i red[4][MT][64];
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int kb = 16 * (lane >> 4);
-  const int8_t* wrow = wq + static_cast<int64_t>(min(n0 + (lane & 15), N - 1)) * K + kb;
-  const int8_t* xrow[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) xrow[t] = xq + static_cast<int64_t>(min(16 * t + (lane & 15), M - 1)) * K + kb;
+// Decode shapes (M <= 64) are bound by streaming wq once from HBM. HBM and the
+// L2 serve a wave's load best when it covers whole 128-byte lines: a load in
+// the MFMA register layout (16 rows x 64 bytes) reaches about 2/3 of the rate
+// of one that covers 4 rows x 256 bytes. So both operands travel by
+// buffer->LDS DMA in 4-row x 256-byte blocks and are read back in the MFMA
+// layout with ds_read_b128.
+//
+// K is walked in 256-byte segments (four MFMA K steps). One segment of a
+// 16-row operand tile is four DMA blocks of 1 KiB, block i holding rows
+// 4i .. 4i+3. Inside a block, DMA lane L (LDS slot L, 16 bytes) fetches row
+// 4i + ((L >> 1) & 3), 16-byte chunk 2 (L >> 3) + (L & 1) of the segment; the
+// blocks sit kDecBlock = 1152 bytes apart. A fragment read of K step t has
+// lanes 0..31 on 16 rows x chunks 4t, 4t+1 (lanes 32..63: 4t+2, 4t+3); with
+// this placement those 32 lanes hit 32 distinct 16-byte slots of a 512-byte
+// window, so the read is bank-conflict free.
+//
+// A workgroup of four waves owns NT tiles of 16 output channels and all MT
+// token tiles. Per segment each wave issues block `wave` of every operand tile
+// (NT + MT DMA instructions), and computes K step `wave` of the segment for
+// all NT x MT output tiles; the four partial accumulators are summed through
+// LDS at the end. Segments go through an R-stage LDS ring, R - 1 in flight.
+constexpr int kDecWaves = 4;
+constexpr int kDecSeg = 256;                 // K bytes per segment
+constexpr int kDecBlock = 1152;              // LDS distance between the DMA blocks of one tile
+constexpr int kDecTile = 4 * kDecBlock;      // LDS bytes of one 16-row operand tile, one segment
 
-  const int steps = K >> 6;                       // 64-byte K steps
-  const int s0 = (steps * wid) >> 2, s1 = (steps * (wid + 1)) >> 2;
-  v4i acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
-
-  constexpr int U = 8;
-  int s = s0;
-  for (; s + U <= s1; s += U) {
-    v4i a[U], b[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + (s + u) * 64));
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) b[u][t] = *reinterpret_cast<const v4i*>(xrow[t] + (s + u) * 64);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][t], acc[t], 0, 0, 0);
-  }
-  for (; s < s1; ++s) {
-    const v4i a = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + s * 64));
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const v4i b = *reinterpret_cast<const v4i*>(xrow[t] + s * 64);
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) red[wid][t][lane] = acc[t];
-  __syncthreads();
-  // wave w finishes m-tiles t = w, w + 4, ...
-  for (int t = wid; t < MT; t += 4) {
-    const v4i tot = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
-    const int m = 16 * t + (lane & 15);
-    const int n = n0 + 4 * (lane >> 4);
-    if (m < M && n < N) store4<YDT>(y, N, m, n, tot, (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
-  }
+// Byte offset, inside a 16-row operand tile, fetched by DMA lane `lane` of block `blk`.
+__device__ __forceinline__ uint32_t dec_src(int lane, int blk, int K) {
+  const int row = 4 * blk + ((lane >> 1) & 3);
+  const int chunk = 2 * (lane >> 3) + (lane & 1);
+  return static_cast<uint32_t>(row * K + 16 * chunk);
 }
 
-// ----------------------------------------------------------------------------- dispatch
+// LDS offset, inside one operand tile, of the fragment lane `lane` reads for K step t.
+__device__ __forceinline__ int dec_frag(int lane, int t) {
+  const int r = lane & 15, c = 4 * t + (lane >> 4);
+  return kDecBlock * (r >> 2) + 16 * (8 * (c >> 1) + 2 * (r & 3) + (c & 1));
+}
+
+// s_waitcnt immediate: vmcnt(n), lgkmcnt(0), expcnt not waited on.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Buffer resource over `bytes` bytes at `base`; loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const int8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+
+// Fragment reads written in asm: at the top of the ring loop the compiler no
+// longer knows which stage each outstanding DMA writes and would drain them
+// all (vmcnt(0)) before a plain LDS read. The DMA data is already covered by
+// the explicit vmcnt wait ahead of the stage barrier; each asm statement waits
+// for its own reads before its outputs are used.
+template <int N>
+__device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[N]) {
+  int i = 0;
+#pragma unroll
+  for (; i + 4 <= N; i += 4)
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[i]), "=&v"(r[i + 1]), "=&v"(r[i + 2]), "=&v"(r[i + 3])
+        : "v"(a[i]), "v"(a[i + 1]), "v"(a[i + 2]), "v"(a[i + 3])
+        : "memory");
+#pragma unroll
+  for (; i + 2 <= N; i += 2)
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[i]), "=&v"(r[i + 1])
+                 : "v"(a[i]), "v"(a[i + 1])
+                 : "memory");
+#pragma unroll
+  for (; i < N; ++i)
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[i]) : "v"(a[i]) : "memory");
+}
+
+template <int NT, int MT, int R, int YDT>
+__global__ __launch_bounds__(64 * kDecWaves) void k_gemm_skinny(const int8_t* __restrict__ xq,
+                                                                const float* __restrict__ xs,
+                                                                const int8_t* __restrict__ wq,
+                                                                const float* __restrict__ ws,
+                                                                const float* __restrict__ bias, void* __restrict__ y,
+                                                                int M, int N, int K) {
+  static_assert(R >= 3 && R <= 8, "ring depth");
+  constexpr int kStage = (NT + MT) * kDecTile;
+  constexpr int kPerWave = NT + MT;                           // DMA instructions per wave per segment
+  static_assert(kStage >= NT * MT * 1024, "a stage holds one wave's partial accumulators");
+  // One array per stage: the compiler then knows which DMA each LDS access depends on.
+  __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t st1[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t st2[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t st3[R > 3 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st4[R > 4 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st5[R > 5 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st6[R > 6 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st7[R > 7 ? kStage : 16];
+  auto stage = [&](auto k) -> int8_t* {
+    constexpr int i = decltype(k)::value;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return st2;
+    else if constexpr (i == 3) return st3;
+    else if constexpr (i == 4) return st4;
+    else if constexpr (i == 5) return st5;
+    else if constexpr (i == 6) return st6;
+    else return st7;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * (16 * NT);
+  const int rows_w = min(16 * NT, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc_n(wq + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(rows_w * K));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc_n(xq, static_cast<uint32_t>(M * K));
+  const uint32_t src = dec_src(lane, wid, K);
+  const int frag = dec_frag(lane, wid);
+  const int steps = K >> 6;
+  const int segs = (steps + 3) >> 2;
+
+  // Loads of a segment past the end use an offset beyond every buffer: they
+  // return zeros without touching memory, so the loop needs no branches around
+  // its loads (the compiler then keeps exact wait counts). Within the last
+  // segment, K steps past K read bytes of the next row (or zeros) and are
+  // skipped by the wave that owns them.
+  constexpr int kNowhere = 0x40000000;
+  auto issue = [&](auto k, int seg) {
+    const int so = seg < segs ? seg * kDecSeg : kNowhere;
+    int8_t* stg = stage(k);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(stg + j * kDecTile + wid * kDecBlock), 16,
+                                               src + static_cast<uint32_t>(16 * j * K), so, 0, 0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stg + (NT + t) * kDecTile + wid * kDecBlock), 16,
+                                               src + static_cast<uint32_t>(16 * t * K), so, 0, 0);
+  };
+
+  v4i acc[NT][MT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = v4i{0, 0, 0, 0};
+
+  // prologue: segments 0 .. R-2, in order (the waits count loads in issue order;
+  // the stages being distinct objects, the compiler could otherwise interleave them)
+#define SQ_DEC_PRO(I) \
+  if constexpr (I < R - 1) { issue(std::integral_constant<int, I>{}, I); memory_opaque(); }
+  SQ_DEC_PRO(0) SQ_DEC_PRO(1) SQ_DEC_PRO(2) SQ_DEC_PRO(3) SQ_DEC_PRO(4) SQ_DEC_PRO(5) SQ_DEC_PRO(6)
+#undef SQ_DEC_PRO
+
+  auto step = [&](auto k, int seg) {
+    constexpr int kk = decltype(k)::value;
+    // wait for this wave's loads of `seg`, then for everyone's DMA
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * kPerWave));
+    stage_barrier();
+    issue(std::integral_constant<int, (kk + R - 1) % R>{}, seg + R - 1);
+    if (4 * seg + wid < steps) {
+      const uint32_t base = lds_addr(stage(k)) + frag;
+      uint32_t addr[NT + MT];
+#pragma unroll
+      for (int i = 0; i < NT + MT; ++i) addr[i] = base + i * kDecTile;
+      v4i f[NT + MT];                                         // NT wq fragments, then MT xq fragments
+      lds_read_frags(f, addr);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[j][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[j], f[NT + t], acc[j][t], 0, 0, 0);
+    }
+  };
+  // Whole rounds of R steps in the loop, the remainder after it: with no
+  // conditional step inside the loop body, no path through it skips a refill,
+  // and the explicit waits stay the only ones the compiler needs.
+  int base = 0;
+  for (; base + R <= segs; base += R) {
+#define SQ_DEC_STEP(I) \
+  if constexpr (I < R) step(std::integral_constant<int, I>{}, base + I);
+    SQ_DEC_STEP(0) SQ_DEC_STEP(1) SQ_DEC_STEP(2) SQ_DEC_STEP(3) SQ_DEC_STEP(4) SQ_DEC_STEP(5) SQ_DEC_STEP(6)
+    SQ_DEC_STEP(7)
+#undef SQ_DEC_STEP
+  }
+#define SQ_DEC_TAIL(I) \
+  if constexpr (I < R - 1) { if (base + I < segs) step(std::integral_constant<int, I>{}, base + I); }
+  SQ_DEC_TAIL(0) SQ_DEC_TAIL(1) SQ_DEC_TAIL(2) SQ_DEC_TAIL(3) SQ_DEC_TAIL(4) SQ_DEC_TAIL(5) SQ_DEC_TAIL(6)
+#undef SQ_DEC_TAIL
+
+  // sum the four waves' partials: waves 1..3 park theirs in stages 0..2
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  stage_barrier();
+  auto park = [&](int8_t* stg) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) reinterpret_cast<v4i*>(stg)[(j * MT + t) * 64 + lane] = acc[j][t];
+  };
+  if (wid == 1) park(st0);
+  else if (wid == 2) park(st1);
+  else if (wid == 3) park(st2);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  stage_barrier();
+  if (wid != 0) return;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int i = (j * MT + t) * 64 + lane;
+      acc[j][t] += reinterpret_cast<const v4i*>(st0)[i] + reinterpret_cast<const v4i*>(st1)[i] +
+                   reinterpret_cast<const v4i*>(st2)[i];
+    }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + (lane & 15);
+    if (m >= M) continue;
+    const float xsm = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + 16 * j + 4 * (lane >> 4);
+      if (n < N) store4<YDT>(y, N, m, n, acc[j][t], xsm, ws, bias);
+    }
+  }
+}
 
 namespace {
 
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) {
-    const dim3 grid((g.N + 15) / 16);
+    // Channel tiles per workgroup (NT): more tiles share each xq segment,
+    // fewer tiles give more workgroups to spread over the CUs. Measured on
+    // K = 9216, N = 9216 / 36864.
     const int mt = (g.M + 15) / 16;
-#define SQ_SKINNY(MTV)                                                                                       \
-  case MTV:                                                                                                  \
-    hipLaunchKernelGGL((k_gemm_skinny<MTV, YDT>), grid, dim3(256), 0, st, g.xq, g.x_scale, g.wq, g.w_scale, \
-                       g.bias, g.y, g.M, g.N, g.K);                                                          \
-    break;
-    switch (mt) {
-      SQ_SKINNY(1) SQ_SKINNY(2) SQ_SKINNY(3) SQ_SKINNY(4)
-      default: return hipErrorInvalidValue;
-    }
+    const int nt = mt == 1 ? 1 : mt == 2 ? (g.N >= 16384 ? 2 : 4) : 3;
+    const dim3 grid((g.N + 16 * nt - 1) / (16 * nt));
+#define SQ_SKINNY(MTV, NTV)                                                                                 \
+  if (mt == MTV && nt == NTV) {                                                                             \
+    hipLaunchKernelGGL((k_gemm_skinny<NTV, MTV, 4, YDT>), grid, dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale, \
+                       g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
+    return hipGetLastError();                                                                               \
+  }
+    SQ_SKINNY(1, 1) SQ_SKINNY(2, 2) SQ_SKINNY(2, 4) SQ_SKINNY(3, 3) SQ_SKINNY(4, 3)
 #undef SQ_SKINNY
-    return hipGetLastError();
+    return hipErrorInvalidValue;
   }
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
