@@ -156,10 +156,14 @@ __device__ __forceinline__ void read_frags(const int8_t* la, const int8_t* lb, i
 // between MFMAs of the current one (the MFMAs only need registers read a step
 // earlier), and nothing crosses the end of the step -- the compiler would
 // otherwise hoist the next step's MFMAs above the stage barrier, right behind
-// the reads they depend on.
+// the reads they depend on. The step's DMA instructions are spread over the
+// first MFMAs as well: issued together right after the barrier, the eight
+// waves' DMAs queue at the CU's address unit and stall the waves behind them.
 __device__ __forceinline__ void interleave_reads_with_mfma() {
+  static_assert(2 * kDmaPerWave <= (TI + TJ + 2) / 3, "one DMA per three fragment reads");
 #pragma unroll
   for (int i = 0; i < TI + TJ; ++i) {
+    if (i % 3 == 0 && i / 3 < 2 * kDmaPerWave) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 DMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
   }
@@ -258,9 +262,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
     __builtin_amdgcn_s_waitcnt(0x0078); /* vmcnt(8) lgkmcnt(0) */       \
     stage_barrier();                                                    \
     const int kn = min((kt + 4) * kSlice, last);                        \
+    __builtin_amdgcn_sched_barrier(0);                                  \
     issue_slice(ra, LA_FREE, a_off, kn, wid);                           \
     issue_slice(rb, LB_FREE, b_off, kn, wid);                           \
-    __builtin_amdgcn_sched_barrier(0);                                  \
     read_frags(LA_NEXT, LB_NEXT, a_rd, b_rd, FN);                       \
     mma(FC, acc);                                                       \
     interleave_reads_with_mfma();                                       \

@@ -110,14 +110,73 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
   }
 }
 
-// y of vector i of a raw row for the NONE norm: x, or fl32(x * gamma).
+// The per-column factors of the thread's own columns (vectors t, t + THREADS,
+// ...), kept for the workgroup's lifetime: a row quantiser reads them for
+// every element of every row, twice, which from L2 costs four times the HBM
+// bytes of a 16-bit row. Vectors [0, GREG) stay in registers, [GREG, GREG +
+// GLDS) in LDS (each thread reads back only what it wrote, so no barrier is
+// involved), the rest are re-read from memory.
+template <int NV, int THREADS, int GREG, int GLDS>
+struct ColVec {
+  static_assert(GREG + GLDS <= NV, "column vector split");
+  float r[GREG > 0 ? GREG : 1][8];
+  float4* lds;                                  // [GLDS][2][THREADS]
+  const float* __restrict__ g;
+  __device__ __forceinline__ void init(const float* __restrict__ gamma, int nvec, float4* lds_mem) {
+    g = gamma;
+    lds = lds_mem;
+    if (!gamma) return;
+#pragma unroll
+    for (int i = 0; i < GREG + GLDS; ++i) {
+      const int vi = threadIdx.x + i * THREADS;
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (vi < nvec) load8_f32(gamma + 8 * vi, v);
+      if (i < GREG) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[i < GREG ? i : 0][e] = v[e];
+      } else {
+        lds[(2 * (i - GREG)) * THREADS + threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
+        lds[(2 * (i - GREG) + 1) * THREADS + threadIdx.x] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+  // factors of vector i (a compile-time index after unrolling)
+  __device__ __forceinline__ void get(int i, float v[8]) const {
+    if (i < GREG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = r[i < GREG ? i : 0][e];
+    } else if (i < GREG + GLDS) {
+      const float4 a = lds[(2 * (i - GREG)) * THREADS + threadIdx.x];
+      const float4 b = lds[(2 * (i - GREG) + 1) * THREADS + threadIdx.x];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      load8_f32(g + 8 * (threadIdx.x + i * THREADS), v);
+    }
+  }
+};
+
+// Split of the column factors for a row layout: as many vectors in registers
+// as fit beside the raw row within 128 VGPRs (two 512-thread or one
+// 1024-thread workgroup per CU; the rest of the quantiser takes about
+// 48 + NV), then LDS up to the workgroup's share (32 / 64 / 128 KiB for
+// 256 / 512 / 1024 threads), then memory.
 template <typename T, int NV, int THREADS>
-__device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i, const float* __restrict__ gamma,
-                                       float y[8]) {
+struct ColSplit {
+  static constexpr int kRaw = NV * 2 * Storage<T>::kBytes;
+  static constexpr int kFree = (128 - kRaw - 48 - NV) / 8;
+  static constexpr int kReg = kFree < 0 ? 0 : (kFree < NV ? kFree : NV);
+  static constexpr int kLdsCap = (THREADS >= 1024 ? 131072 : THREADS >= 512 ? 65536 : 32768) / (THREADS * 32);
+  static constexpr int kLds = NV - kReg < kLdsCap ? NV - kReg : kLdsCap;
+};
+
+// y of vector i of a raw row for the NONE norm: x, or fl32(x * gamma).
+template <typename T, int NV, int THREADS, int GREG, int GLDS>
+__device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
+                                       const ColVec<NV, THREADS, GREG, GLDS>& gv, float y[8]) {
   widen8<T>(raw.r[i], y);
-  if (gamma) {
+  if (gv.g) {
     float g[8];
-    load8_f32(gamma + 8 * (threadIdx.x + i * THREADS), g);
+    gv.get(i, g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = mul_rn(y[e], g[e]);
   }
@@ -131,9 +190,10 @@ __device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
 //        is refilled right after its codes are written.
 //  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
 //        normalise in place, then max and codes.
-template <typename T, int NORM, int NV, int THREADS>
+template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
 __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x, int64_t row,
                                              int64_t next, int M, int K, const float* __restrict__ gamma,
+                                             const ColVec<NV, THREADS, GREG, GLDS>& gv,
                                              const float* __restrict__ beta, float eps, int8_t* __restrict__ xq,
                                              float* __restrict__ x_scale, double* red) {
   const int nvec = K >> 3;
@@ -152,7 +212,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
       pm[i] = 0.0f;
       if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
         float y[8];
-        none_y<T, NV, THREADS>(raw, i, gamma, y);
+        none_y(raw, i, gv, y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) pm[i] = fmaxf(pm[i], fabsf(y[e]));
       }
@@ -164,7 +224,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
     const float step = int8_step(amax);
     if (threadIdx.x == 0) x_scale[row] = step;
     const Quantizer qz(step);
-    // recompute x * gamma below rather than keep pass one's 8*NV products (or gamma) in registers
+    // recompute x * gamma below rather than keep pass one's 8*NV products in registers
 #pragma unroll
     for (int i = 0; i < NV; ++i) opaque(raw.r[i].a);
     memory_opaque();
@@ -173,7 +233,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
       const int vi = threadIdx.x + i * THREADS;
       if (vi < nvec) {
         float y[8];
-        none_y<T, NV, THREADS>(raw, i, gamma, y);
+        none_y(raw, i, gv, y);
         *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(y);
         if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
       }
@@ -228,11 +288,18 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
                                                         const float* __restrict__ beta, float eps,
                                                         int8_t* __restrict__ xq, float* __restrict__ x_scale) {
   __shared__ double red[THREADS / kWave];
+  // NONE keeps its column factors for the workgroup's lifetime (the norms read
+  // gamma / beta once per row)
+  constexpr int kReg = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kReg : 0;
+  constexpr int kLds = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kLds : 0;
+  __shared__ float4 gl[kLds > 0 ? 2 * kLds * THREADS : 1];
+  ColVec<NV, THREADS, kReg, kLds> gv;
   const int64_t G = gridDim.x;
   RawRow<T, NV, THREADS> raw;
   raw.load(x, blockIdx.x, K);
+  gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
   for (int64_t row = blockIdx.x; row < M; row += G)
-    quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, beta, eps, xq, x_scale, red);
+    quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red);
 }
 
 // Calibration with a norm: workgroups stride over rows, normalise each with the
