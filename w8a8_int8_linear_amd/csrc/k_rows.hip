@@ -35,7 +35,8 @@ struct RawRow {
 // mean) and rounded once to binary32; rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
 template <int NORM, int NV, int THREADS>
 __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const float* __restrict__ gamma,
-                                              const float* __restrict__ beta, float eps, double* red) {
+                                              const float* __restrict__ beta, float eps, RedRing<THREADS>& red,
+                                              int& rk) {
   const int nvec = K >> 3;
   float mu = 0.0f, r = 1.0f;
   if constexpr (NORM == SQ_NORM_LAYERNORM) {
@@ -50,7 +51,7 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
     double s1 = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) s1 += p1[i];
-    s1 = block_sum<THREADS>(s1, red);
+    s1 = block_sum<THREADS>(s1, red.at(rk++));
     const double mean = s1 / static_cast<double>(K);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -71,7 +72,7 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
     double s2 = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) s2 += p2[i];
-    s2 = block_sum<THREADS>(s2, red);
+    s2 = block_sum<THREADS>(s2, red.at(rk++));
     mu = static_cast<float>(mean);
     r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
   } else if constexpr (NORM == SQ_NORM_RMSNORM) {
@@ -88,7 +89,7 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
     double s2 = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) s2 += p2[i];
-    s2 = block_sum<THREADS>(s2, red);
+    s2 = block_sum<THREADS>(s2, red.at(rk++));
     r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
   }
 #pragma unroll
@@ -191,11 +192,12 @@ __device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
 //  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
 //        normalise in place, then max and codes.
 template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
-__device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x, int64_t row,
-                                             int64_t next, int M, int K, const float* __restrict__ gamma,
+__device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
+                                             int64_t row, int64_t next, int M, int K,
+                                             const float* __restrict__ gamma,
                                              const ColVec<NV, THREADS, GREG, GLDS>& gv,
                                              const float* __restrict__ beta, float eps, int8_t* __restrict__ xq,
-                                             float* __restrict__ x_scale, double* red) {
+                                             float* __restrict__ x_scale, RedRing<THREADS>& red, int& rk) {
   const int nvec = K >> 3;
   constexpr int B = Storage<T>::kBytes;
   int8_t* qrow = xq + row * K;
@@ -220,7 +222,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
-    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red));
+    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
     const float step = int8_step(amax);
     if (threadIdx.x == 0) x_scale[row] = step;
     const Quantizer qz(step);
@@ -256,7 +258,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
         if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
       }
     }
-    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red);
+    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
     float pm[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -267,7 +269,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
-    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red));
+    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
     const float step = int8_step(amax);
     if (threadIdx.x == 0) x_scale[row] = step;
     const Quantizer qz(step);
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, float eps,
                                                         int8_t* __restrict__ xq, float* __restrict__ x_scale) {
-  __shared__ double red[THREADS / kWave];
+  __shared__ RedRing<THREADS> red;
   // NONE keeps its column factors for the workgroup's lifetime (the norms read
   // gamma / beta once per row)
   constexpr int kReg = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kReg : 0;
@@ -298,8 +300,9 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
   RawRow<T, NV, THREADS> raw;
   raw.load(x, blockIdx.x, K);
   gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
+  int rk = 0;
   for (int64_t row = blockIdx.x; row < M; row += G)
-    quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red);
+    quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk);
 }
 
 // Calibration with a norm: workgroups stride over rows, normalise each with the
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ 
                                                        const float* __restrict__ gamma,
                                                        const float* __restrict__ beta, float eps,
                                                        float* __restrict__ absmax) {
-  __shared__ double red[THREADS / kWave];
+  __shared__ RedRing<THREADS> red;
+  int rk = 0;
   const int nvec = K >> 3;
   float cm[NV][8];
 #pragma unroll
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ 
         for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
       }
     }
-    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red);
+    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll

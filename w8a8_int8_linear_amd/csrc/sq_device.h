@@ -114,26 +114,75 @@ __device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
 }
 
 // ----------------------------------------------------------------------------- reductions
+// Wave reductions by DPP lane moves (no LDS round trips): inside each 16-lane
+// row, exchange with lane ^ 1, ^ 2, then the mirrored lane of the half row and
+// of the row; every step combines two equal-sized partial results in an order
+// that is the same on both lanes, so all 16 lanes end with identical bits. The
+// four row results are then combined in a fixed order from uniform values.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = dpp_move<CTRL>(static_cast<int>(u & 0xffffffffu));
+  const int hi = dpp_move<CTRL>(static_cast<int>(u >> 32));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(dpp_move<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ double read_lane(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+constexpr int kDppXor1 = 0xB1;           // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;           // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;    // row_half_mirror
+constexpr int kDppMirror = 0x140;        // row_mirror
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_move<kDppXor1>(v);
+  v += dpp_move<kDppXor2>(v);
+  v += dpp_move<kDppHalfMirror>(v);
+  v += dpp_move<kDppMirror>(v);
+  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_move<kDppXor1>(v));
+  v = fmaxf(v, dpp_move<kDppXor2>(v));
+  v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kDppMirror>(v));
+  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
-// Block-wide sum in a fixed order (deterministic run to run). `red` holds >= THREADS/64 doubles.
+// Workgroup reductions with one barrier each: wave results go to LDS, and
+// every thread combines them in a fixed order (deterministic run to run).
+// Successive reductions must alternate between two buffers (RedRing): a
+// buffer is written again only two reductions later, after a barrier that
+// every thread reaches only once it has read the buffer's previous contents.
+template <int THREADS>
+struct RedRing {
+  double buf[2][THREADS / kWave];
+  __device__ __forceinline__ double* at(int k) { return buf[k & 1]; }
+};
+
 template <int THREADS>
 __device__ __forceinline__ double block_sum(double v, double* red) {
   constexpr int kWaves = THREADS / kWave;
   v = wave_sum(v);
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) red[wid] = v;
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
   double t = 0.0;
 #pragma unroll
@@ -145,9 +194,7 @@ template <int THREADS>
 __device__ __forceinline__ float block_max(float v, float* red) {
   constexpr int kWaves = THREADS / kWave;
   v = wave_max(v);
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) red[wid] = v;
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
   float t = red[0];
 #pragma unroll
