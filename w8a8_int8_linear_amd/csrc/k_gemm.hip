@@ -3,15 +3,16 @@
 //   y[m, n] = cvt(fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n]) (+ bias[n])),
 //   acc[m, n] = sum_k xq[m, k] * wq[n, k]   (both operands K-contiguous)
 //
-// Two kernels:
+// Kernels:
 //  * k_gemm_tile  -- prefill shapes. 256x256 output tile per workgroup of eight
 //    waves (2 x 4, 128 x 64 each: two waves per SIMD, accumulators in VGPRs), K
-//    staged through LDS in 64-byte slices by buffer->LDS DMA
-//    (buffer_load_dwordx4 ... lds) into a 4-stage ring with three slices in
-//    flight, computed with v_mfma_i32_16x16x64_i8. LDS rows are swizzled in
-//    16-byte chunks so the fragment reads are bank-conflict free. Workgroups are
-//    mapped to tiles XCD by XCD and in column groups, so tiles that share
-//    operand rows run at the same time on the same L2.
+//    staged through LDS 128 bytes at a time by buffer->LDS DMA
+//    (buffer_load_dwordx4 ... lds) into a 2-stage ring, computed with
+//    v_mfma_i32_16x16x64_i8. LDS rows are swizzled in 16-byte chunks so the
+//    fragment reads are bank-conflict free. Workgroups are mapped to tiles XCD
+//    by XCD and in column groups, so tiles that share operand rows run at the
+//    same time on the same L2. k_gemm_tile_k64 is the same tile with 64-byte
+//    slices in a 4-stage ring, for K % 128 == 64.
 //  * k_gemm_skinny -- decode shapes (M <= 64), bound by streaming wq from HBM
 //    (described at the kernel).
 //
@@ -179,7 +180,7 @@ __device__ __forceinline__ void mma(const Frags& f, v4i (&acc)[TI][TJ]) {
 }
 
 template <int YDT>
-__global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+__global__ __launch_bounds__(512, 1) void k_gemm_tile_k64(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                                       const int8_t* __restrict__ wq, const float* __restrict__ ws,
                                                       const float* __restrict__ bias, void* __restrict__ y,
                                                       int M, int N, int K, int tiles_m, int tiles_n, int group) {
@@ -281,6 +282,162 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   if (kt < nk) SQ_STEP(f1, f0, lA2, lB2, lA1, lB1)
   if (kt < nk) SQ_STEP(f0, f1, lA3, lB3, lA2, lB2)
 #undef SQ_STEP
+  __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): no DMA into LDS outlives the loop
+
+  // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int m = m0 + wm + 16 * i + (lane & 15);
+    if (m >= M) continue;
+    const float xsm = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+      if (n < N) store4<YDT>(y, N, m, n, acc[i][j], xsm, ws, bias);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- tiled kernel, 128-byte stages
+
+// The same tile and wave layout, with K staged 128 bytes (two MFMA K steps) at
+// a time in a 2-stage ring: each DMA instruction then fetches 8 rows x 128
+// bytes, whole L2 lines, where a 64-byte stage can only fetch half lines
+// (16 rows x 64 bytes). Measured on the MT-NLG shapes: 2810 against 2550
+// TOPS. The barrier is needed once per stage, i.e. every second K step.
+// Requires K % 128 == 0 (the 64-byte kernel takes the other case).
+constexpr int kSlice2 = 128;                         // K bytes per stage
+constexpr int kStage2Bytes = kTile * kSlice2;        // one operand, one stage: 32 KiB
+constexpr int kDma2PerWave = kStage2Bytes / 1024 / 8;   // DMA instructions (8 rows x 128 B) per wave per operand: 4
+
+// LDS layout of a stage: row r at r * 128, its 16-byte chunk c at slot
+// c ^ swz2(r). Lanes 0..31 of a fragment read cover 16 rows x chunks 4t, 4t+1;
+// rows r, r + 4, r + 8, r + 12 share a 512-byte window position, so they get
+// slot offsets 0, 2, 4, 6 and the 32 lanes hit 32 distinct slots.
+__device__ __forceinline__ int swz2(int r) { return ((r >> 2) & 3) << 1; }
+
+__device__ __forceinline__ void issue_stage2(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds,
+                                             const uint32_t (&off)[kDma2PerWave], int k0, int wid) {
+#pragma unroll
+  for (int i = 0; i < kDma2PerWave; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wid * kDma2PerWave + i) * 1024), 16, off[i], k0,
+                                             0, 0);
+}
+
+// Fragments of K step t (0 or 1) of a stage.
+__device__ __forceinline__ void read_frags2(const int8_t* la, const int8_t* lb, const int (&a_rd)[2],
+                                            const int (&b_rd)[2], int t, Frags& f) {
+#pragma unroll
+  for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const v4i*>(la + a_rd[t] + i * 16 * kSlice2);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) f.b[j] = *reinterpret_cast<const v4i*>(lb + b_rd[t] + j * 16 * kSlice2);
+}
+
+// As interleave_reads_with_mfma; on the step that refills a stage, its eight
+// DMA instructions go out two at a time between the first MFMAs.
+__device__ __forceinline__ void interleave2(bool with_dma) {
+  static_assert(2 * kDma2PerWave <= 2 * ((TI + TJ + 2) / 3), "two DMAs per three fragment reads");
+#pragma unroll
+  for (int i = 0; i < TI + TJ; ++i) {
+    if (with_dma && i % 3 == 0 && i / 3 < kDma2PerWave) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - 2 * (TI + TJ), 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int YDT>
+__global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                      const int8_t* __restrict__ wq, const float* __restrict__ ws,
+                                                      const float* __restrict__ bias, void* __restrict__ y, int M,
+                                                      int N, int K, int tiles_m, int tiles_n, int group) {
+  __shared__ __attribute__((aligned(1024))) int8_t lA0[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lA1[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB0[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB1[kStage2Bytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS bases stay scalar
+  int tm, tn;
+  map_tile(blockIdx.x, tiles_m * tiles_n, tiles_m, group, tm, tn);
+  const int m0 = tm * kTile, n0 = tn * kTile;
+
+  // DMA lanes: instruction i of wave w fills LDS rows (w*4 + i)*8 .. +8 of one
+  // operand; lane -> row lane / 8, slot lane % 8, which holds chunk
+  // slot ^ swz2(row). Rows past M or N re-read the last row (never stored).
+  uint32_t a_off[kDma2PerWave], b_off[kDma2PerWave];
+#pragma unroll
+  for (int i = 0; i < kDma2PerWave; ++i) {
+    const int r = (wid * kDma2PerWave + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz2(r);
+    a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
+    b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
+  }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
+
+  // Fragment reads of K step t: row R = base + 16 i + lane % 16, chunk 4 t + lane / 16.
+  const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
+  const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
+  int a_rd[2], b_rd[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int c = 4 * t + (lane >> 4);
+    a_rd[t] = rra * kSlice2 + 16 * (c ^ swz2(rra));
+    b_rd[t] = rrb * kSlice2 + 16 * (c ^ swz2(rrb));
+  }
+
+  v4i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  // Stage S holds K steps 2S and 2S+1. Entering stage S, the fragments of step
+  // 2S are in registers and stage S+1 is in flight. Step 2S reads the
+  // fragments of step 2S+1 from the same stage and multiplies step 2S. Step
+  // 2S+1 waits for stage S+1 (vmcnt(0): it is the only stage in flight),
+  // lets the barrier make it visible and free stage S's buffer (lgkmcnt(0):
+  // this wave's reads of it are done), refills that buffer with stage S+2,
+  // reads the fragments of step 2S+2 and multiplies step 2S+1. Issue indices
+  // are clamped to the last stage; the final issues are harmless reloads.
+  const int ns = K / kSlice2;
+  const int last = (ns - 1) * kSlice2;
+  // in stage order: the waits count DMAs in issue order (see the 64-byte kernel)
+  issue_stage2(ra, lA0, a_off, 0, wid);
+  issue_stage2(rb, lB0, b_off, 0, wid);
+  memory_opaque();
+  issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
+  issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
+  Frags f0, f1;
+  __builtin_amdgcn_s_waitcnt(0x0F78);     // vmcnt(8): stage 0 landed
+  stage_barrier();
+  read_frags2(lA0, lB0, a_rd, b_rd, 0, f0);
+
+#define SQ_STAGE(LA_CUR, LB_CUR, LA_NXT, LB_NXT)                                      \
+  {                                                                                   \
+    read_frags2(LA_CUR, LB_CUR, a_rd, b_rd, 1, f1);                                   \
+    mma(f0, acc);                                                                     \
+    interleave2(false);                                                               \
+    __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0) */                     \
+    stage_barrier();                                                                  \
+    const int kn = min((s + 2) * kSlice2, last);                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    issue_stage2(ra, LA_CUR, a_off, kn, wid);                                         \
+    issue_stage2(rb, LB_CUR, b_off, kn, wid);                                         \
+    read_frags2(LA_NXT, LB_NXT, a_rd, b_rd, 0, f0);                                   \
+    mma(f1, acc);                                                                     \
+    interleave2(true);                                                                \
+    ++s;                                                                              \
+  }
+  int s = 0;
+  for (; s + 2 <= ns;) {
+    SQ_STAGE(lA0, lB0, lA1, lB1)
+    SQ_STAGE(lA1, lB1, lA0, lB0)
+  }
+  if (s < ns) SQ_STAGE(lA0, lB0, lA1, lB1)
+#undef SQ_STAGE
   __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): no DMA into LDS outlives the loop
 
   // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
@@ -549,8 +706,12 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
-  hipLaunchKernelGGL((k_gemm_tile<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
-                     g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  if (g.K % kSlice2 == 0)
+    hipLaunchKernelGGL((k_gemm_tile<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
+                       g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  else
+    hipLaunchKernelGGL((k_gemm_tile_k64<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
+                       g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
   return hipGetLastError();
 }
 
