@@ -42,7 +42,7 @@ def np_or_none(t):
 
 # --------------------------------------------------------------------------- fused norm + quantise
 
-NQ_SHAPES = [(1, 64), (7, 512), (33, 4096), (5, 9216), (3, 20480), (2, 81920), (2, 133120)]
+NQ_SHAPES = [(1, 64), (7, 512), (33, 4096), (5, 9216), (3, 20480), (3, 66560), (2, 81920), (2, 133120)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -79,6 +79,21 @@ def test_norm_quant_edge_rows(dtype):
         check_norm_quant(to_numpy(x), dtype, norm, None, None, 1e-5, host(xq), host(xs), label=f"edge/{dtype}/{norm}")
     q = host(sq.sq_norm_quant(cuda(x), "none")[0])
     assert q[2, :4].tolist() == [127, -4, 2, -4] and not q[0].any() and not q[1].any()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("k", [20480, 66560, 81920])
+def test_norm_quant_none_many_rows(dtype, k):
+    # many rows per workgroup: the raw-row refill and the per-workgroup column
+    # factors (registers / LDS / memory) of every NONE layout
+    m = 600
+    seed = _seed("nqm", dtype, m, k)
+    x = rand_tokens(m, k, dtype, seed, n_outliers=k // 2000, outlier_scale=100.0)
+    gamma, _ = params(k, seed + 1, "none")
+    xq, xs = sq.sq_norm_quant(cuda(x), "none", cuda(gamma), None, 1e-5)
+    torch.cuda.synchronize()
+    check_norm_quant(to_numpy(x), dtype, "none", np_or_none(gamma), None, 1e-5, host(xq), host(xs),
+                     label=f"{dtype}/none/{m}x{k}")
 
 
 def test_norm_quant_repeatable():

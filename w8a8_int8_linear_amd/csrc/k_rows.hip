@@ -163,10 +163,15 @@ struct ColVec {
 // 256 / 512 / 1024 threads), then memory.
 template <typename T, int NV, int THREADS>
 struct ColSplit {
+  // the wide NONE layout (512 threads, more than 6 vectors each) runs one
+  // workgroup per CU: 256 VGPRs per thread and 144 KiB of LDS
+  static constexpr bool kWide = THREADS == 512 && NV > 6;
+  static constexpr int kBudget = kWide ? 256 : 128;
   static constexpr int kRaw = NV * 2 * Storage<T>::kBytes;
-  static constexpr int kFree = (128 - kRaw - 48 - NV) / 8;
+  static constexpr int kFree = (kBudget - kRaw - 48 - NV) / 8;
   static constexpr int kReg = kFree < 0 ? 0 : (kFree < NV ? kFree : NV);
-  static constexpr int kLdsCap = (THREADS >= 1024 ? 131072 : THREADS >= 512 ? 65536 : 32768) / (THREADS * 32);
+  static constexpr int kLdsCap =
+      (kWide ? 147456 : THREADS >= 1024 ? 131072 : THREADS >= 512 ? 65536 : 32768) / (THREADS * 32);
   static constexpr int kLds = NV - kReg < kLdsCap ? NV - kReg : kLdsCap;
 };
 
@@ -473,9 +478,14 @@ namespace {
 
 struct RowCfg { int threads, nv; };
 
-// Smallest (threads, vectors per thread) covering K/8 vectors of the row.
-RowCfg row_cfg(int K) {
+// Smallest (threads, vectors per thread) covering K/8 vectors of the row. The
+// NONE quantiser of 16-bit rows of 65544 .. 81920 columns takes 512 threads x
+// 20 vectors instead of 1024 x 10: one workgroup per CU then holds all of its
+// column factors (13 vectors in registers, 7 in LDS) where the 1024-thread
+// layout has room for 7 of 10.
+RowCfg row_cfg(int K, int norm, int bytes) {
   const int nvec = K >> 3;
+  if (norm == SQ_NORM_NONE && bytes == 2 && nvec > 8192 && nvec <= 10240) return {512, 20};
   static const RowCfg table[] = {{256, 1}, {256, 2}, {256, 3}, {256, 4}, {512, 3},  {512, 4},   {512, 5},
                                  {512, 6}, {1024, 4}, {1024, 6}, {1024, 8}, {1024, 10}, {1024, 13}, {1024, 17}};
   for (const RowCfg& c : table)
@@ -553,7 +563,10 @@ hipError_t dispatch_one(const RowArgs& a, hipStream_t st) {
 
 template <bool CAL, typename T, int NORM>
 hipError_t dispatch_cfg(const RowArgs& a, hipStream_t st) {
-  const RowCfg c = row_cfg(a.K);
+  const RowCfg c = row_cfg(a.K, NORM, Storage<T>::kBytes);
+  if constexpr (!CAL && NORM == SQ_NORM_NONE && Storage<T>::kBytes == 2) {
+    if (c.threads == 512 && c.nv == 20) return dispatch_one<CAL, T, NORM, 20, 512>(a, st);
+  }
 #define SQ_ROW_CASE(TH, NVV) \
   if (c.threads == TH && c.nv == NVV) return dispatch_one<CAL, T, NORM, NVV, TH>(a, st);
   SQ_ROW_CASE(256, 1) SQ_ROW_CASE(256, 2) SQ_ROW_CASE(256, 3) SQ_ROW_CASE(256, 4)
