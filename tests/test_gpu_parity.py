@@ -157,7 +157,9 @@ GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 
                (600, 700, 4096),
                # decode kernel: every token-tile count, K tails of 64 / 128 / 192 bytes past a 256-byte segment
                (16, 48, 320), (32, 100, 576), (33, 17, 192), (48, 70, 4160), (63, 130, 2112), (64, 2048, 9216),
-               (5, 36, 1984)]
+               (5, 36, 1984),
+               # decode kernel, 144-channel strips (N >= 16384): ragged last strip, K tails
+               (33, 16400, 320), (20, 16384, 1088), (64, 16416, 2112)]
 
 
 @pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -13,8 +13,8 @@
 //    by XCD and in column groups, so tiles that share operand rows run at the
 //    same time on the same L2. k_gemm_tile_k64 is the same tile with 64-byte
 //    slices in a 4-stage ring, for K % 128 == 64.
-//  * k_gemm_skinny -- decode shapes (M <= 64), bound by streaming wq from HBM
-//    (described at the kernel).
+//  * k_gemm_skinny, k_gemm_decode -- decode shapes (M <= 64), bound by
+//    streaming wq from HBM (described at the kernels).
 //
 // MFMA operand order: the A operand (rows = lane % 16) carries 16 rows of wq and
 // the B operand (columns = lane % 16) 16 rows of xq, so the 16x16 result tile
@@ -682,26 +682,194 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_skinny(const int8_t* __
   }
 }
 
+// ----------------------------------------------------------------------------- decode kernel, 128-byte segments
+
+// The decode kernel with the prefill kernel's LDS layout: K in 128-byte
+// segments (two MFMA K steps), operand tiles of 16 rows x 128 bytes (row r at
+// r * 128, chunk c at slot c ^ swz2(r)), and DMA blocks of 8 rows x 128 bytes,
+// two per tile. A workgroup owns NT channel tiles (up to 9: a 144-channel
+// strip, so 36864 channels make exactly 256 workgroups and each xq segment
+// serves NT weight tiles). The four waves split each segment as (K step
+// = wave & 1, channel-tile half = wave >> 1); the two K steps' partials are
+// summed through LDS at the end. Segments go through an R-stage ring.
+constexpr int kDecNowhere = 0x40000000;               // a buffer offset past every operand: loads return zeros
+constexpr int kDec2Seg = 128;
+constexpr int kDec2Tile = 16 * kDec2Seg;             // LDS bytes of one 16-row operand tile
+
+template <int NT, int MT, int R, int YDT>
+__global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __restrict__ xq,
+                                                                const float* __restrict__ xs,
+                                                                const int8_t* __restrict__ wq,
+                                                                const float* __restrict__ ws,
+                                                                const float* __restrict__ bias, void* __restrict__ y,
+                                                                int M, int N, int K) {
+  static_assert(R >= 3 && R <= 8, "ring depth");
+  constexpr int kTiles = NT + MT;
+  constexpr int kWPer = (2 * NT + kDecWaves - 1) / kDecWaves;     // weight DMA blocks per wave per segment
+  constexpr int kXPer = (2 * MT + kDecWaves - 1) / kDecWaves;     // token DMA blocks per wave per segment
+  constexpr int kPerWave = kWPer + kXPer;                          // DMA instructions per wave per segment
+  constexpr bool kSink = (2 * NT) % kDecWaves != 0 || (2 * MT) % kDecWaves != 0;   // padding DMAs need a sink
+  constexpr int kStage = kTiles * kDec2Tile + (kSink ? 1024 : 0);
+  constexpr int NH = (NT + 1) / 2;                               // channel tiles per half (the second may have one fewer)
+  static_assert(kStage >= NH * MT * 1024, "a stage holds one wave's partial accumulators");
+  __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t st1[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t st2[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t st3[R > 3 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st4[R > 4 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st5[R > 5 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st6[R > 6 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st7[R > 7 ? kStage : 16];
+  auto stage = [&](auto k) -> int8_t* {
+    constexpr int i = decltype(k)::value;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return st2;
+    else if constexpr (i == 3) return st3;
+    else if constexpr (i == 4) return st4;
+    else if constexpr (i == 5) return st5;
+    else if constexpr (i == 6) return st6;
+    else return st7;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * (16 * NT);
+  const int rows_w = min(16 * NT, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc_n(wq + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(rows_w * K));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc_n(xq, static_cast<uint32_t>(M * K));
+  const int steps = K >> 6;
+  const int segs = (steps + 1) >> 1;
+
+  // Weight blocks b = wid + 4 i (tile b / 2, rows 8 (b % 2) .. +8 of it), then
+  // token blocks likewise; blocks past the operand's count load nothing into
+  // the sink. (Offsets are recomputed per issue: per-wave tables indexed inside
+  // the lambda make the host compiler drop the kernel's launch stub.)
+  const int rr = lane >> 3;                                     // row within a DMA block
+  const uint32_t lane_src0 = static_cast<uint32_t>(rr * K + 16 * ((lane & 7) ^ swz2(rr)));
+  const uint32_t lane_src1 = static_cast<uint32_t>((8 + rr) * K + 16 * ((lane & 7) ^ swz2(8 + rr)));
+  auto issue = [&](auto k, int seg) {
+    const int so = seg < segs ? seg * kDec2Seg : kDecNowhere;
+    int8_t* stg = stage(k);
+#pragma unroll
+    for (int i = 0; i < kWPer + kXPer; ++i) {
+      const bool w = i < kWPer;
+      const int b = wid + kDecWaves * (w ? i : i - kWPer);
+      const bool real = b < 2 * (w ? NT : MT);
+      const int tile = real ? b >> 1 : 0, half = b & 1;
+      const uint32_t src = static_cast<uint32_t>(16 * tile * K) + (half ? lane_src1 : lane_src0);
+      const int dst = real ? ((w ? 0 : NT) + tile) * kDec2Tile + half * 1024 : kTiles * kDec2Tile;
+      if (w)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(stg + dst), 16, src, real ? so : kDecNowhere, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stg + dst), 16, src, real ? so : kDecNowhere, 0, 0);
+    }
+  };
+
+  // compute share: K step t of each segment, channel tiles [h NH, h NH + NH) (clipped to NT)
+  const int t = wid & 1, h = wid >> 1;
+  const int c = 4 * t + (lane >> 4), r16 = lane & 15;
+  const int frag = r16 * kDec2Seg + 16 * (c ^ swz2(r16));
+  v4i acc[NH][MT];
+#pragma unroll
+  for (int j = 0; j < NH; ++j)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[j][u] = v4i{0, 0, 0, 0};
+
+#define SQ_DEC_PRO(I) \
+  if constexpr (I < R - 1) { issue(std::integral_constant<int, I>{}, I); memory_opaque(); }
+  SQ_DEC_PRO(0) SQ_DEC_PRO(1) SQ_DEC_PRO(2) SQ_DEC_PRO(3) SQ_DEC_PRO(4) SQ_DEC_PRO(5) SQ_DEC_PRO(6)
+#undef SQ_DEC_PRO
+
+  auto step = [&](auto k, int seg) {
+    constexpr int kk = decltype(k)::value;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * kPerWave));
+    stage_barrier();
+    issue(std::integral_constant<int, (kk + R - 1) % R>{}, seg + R - 1);
+    if (2 * seg + t < steps) {
+      const uint32_t base = lds_addr(stage(k)) + frag;
+      uint32_t addr[NH + MT];
+#pragma unroll
+      for (int j = 0; j < NH; ++j) addr[j] = base + min(h * NH + j, NT - 1) * kDec2Tile;
+#pragma unroll
+      for (int u = 0; u < MT; ++u) addr[NH + u] = base + (NT + u) * kDec2Tile;
+      v4i f[NH + MT];
+      lds_read_frags(f, addr);
+#pragma unroll
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[j][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[j], f[NH + u], acc[j][u], 0, 0, 0);
+    }
+  };
+  int base = 0;
+  for (; base + R <= segs; base += R) {
+#define SQ_DEC_STEP(I) \
+  if constexpr (I < R) step(std::integral_constant<int, I>{}, base + I);
+    SQ_DEC_STEP(0) SQ_DEC_STEP(1) SQ_DEC_STEP(2) SQ_DEC_STEP(3) SQ_DEC_STEP(4) SQ_DEC_STEP(5) SQ_DEC_STEP(6)
+    SQ_DEC_STEP(7)
+#undef SQ_DEC_STEP
+  }
+#define SQ_DEC_TAIL(I) \
+  if constexpr (I < R - 1) { if (base + I < segs) step(std::integral_constant<int, I>{}, base + I); }
+  SQ_DEC_TAIL(0) SQ_DEC_TAIL(1) SQ_DEC_TAIL(2) SQ_DEC_TAIL(3) SQ_DEC_TAIL(4) SQ_DEC_TAIL(5) SQ_DEC_TAIL(6)
+#undef SQ_DEC_TAIL
+
+  // K step 1's partials (waves 1, 3) join K step 0's (waves 0, 2) through LDS
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  stage_barrier();
+  int8_t* park = h == 0 ? st0 : st1;
+  if (t == 1) {
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) reinterpret_cast<v4i*>(park)[(j * MT + u) * 64 + lane] = acc[j][u];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  stage_barrier();
+  if (t == 1) return;
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    if (h * NH + j >= NT) continue;                              // uniform
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      const v4i v = acc[j][u] + reinterpret_cast<const v4i*>(park)[(j * MT + u) * 64 + lane];
+      const int m = 16 * u + (lane & 15);
+      const int n = n0 + 16 * (h * NH + j) + 4 * (lane >> 4);
+      if (m < M && n < N) store4<YDT>(y, N, m, n, v, (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
+    }
+  }
+}
+
 namespace {
 
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) {
-    // Channel tiles per workgroup (NT): more tiles share each xq segment,
-    // fewer tiles give more workgroups to spread over the CUs. Measured on
+    // One token tile: the 256-byte-segment kernel, one channel tile per
+    // workgroup. More token tiles: the 128-byte-segment kernel with up to 9
+    // channel tiles per workgroup, so that each token segment serves many
+    // weight tiles (fewer at small N, to keep every CU busy). Measured on
     // K = 9216, N = 9216 / 36864.
     const int mt = (g.M + 15) / 16;
-    const int nt = mt == 1 ? 1 : mt == 2 ? (g.N >= 16384 ? 2 : 4) : 3;
-    const dim3 grid((g.N + 16 * nt - 1) / (16 * nt));
-#define SQ_SKINNY(MTV, NTV)                                                                                 \
-  if (mt == MTV && nt == NTV) {                                                                             \
-    hipLaunchKernelGGL((k_gemm_skinny<NTV, MTV, 4, YDT>), grid, dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale, \
-                       g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
-    return hipGetLastError();                                                                               \
+    const bool wide = g.N >= 16384;
+#define SQ_DECODE(KERN, NTV)                                                                                 \
+  {                                                                                                          \
+    hipLaunchKernelGGL(KERN, dim3((g.N + 16 * NTV - 1) / (16 * NTV)), dim3(64 * kDecWaves), 0, st, g.xq,    \
+                       g.x_scale, g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                              \
+    return hipGetLastError();                                                                                \
   }
-    SQ_SKINNY(1, 1) SQ_SKINNY(2, 2) SQ_SKINNY(2, 4) SQ_SKINNY(3, 3) SQ_SKINNY(4, 3)
-#undef SQ_SKINNY
-    return hipErrorInvalidValue;
+    if (mt == 1) SQ_DECODE((k_gemm_skinny<1, 1, 4, YDT>), 1)
+    if (mt == 2) {
+      if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT>), 9)
+      SQ_DECODE((k_gemm_decode<4, 2, 6, YDT>), 4)
+    }
+    if (mt == 3) {
+      if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT>), 9)
+      SQ_DECODE((k_gemm_decode<3, 3, 5, YDT>), 3)
+    }
+    if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT>), 9)
+    SQ_DECODE((k_gemm_decode<3, 4, 5, YDT>), 3)
+#undef SQ_DECODE
   }
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
