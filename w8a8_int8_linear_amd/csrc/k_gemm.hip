@@ -845,8 +845,8 @@ namespace {
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) {
-    // One token tile: the 256-byte-segment kernel, one channel tile per
-    // workgroup. More token tiles: the 128-byte-segment kernel with up to 9
+    // Up to 8 tokens: the 256-byte-segment kernel, one channel tile per
+    // workgroup. More tokens: the 128-byte-segment kernel with up to 9
     // channel tiles per workgroup, so that each token segment serves many
     // weight tiles (fewer at small N, to keep every CU busy). Measured on
     // K = 9216, N = 9216 / 36864.
@@ -858,7 +858,11 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
                        g.x_scale, g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                              \
     return hipGetLastError();                                                                                \
   }
-    if (mt == 1) SQ_DECODE((k_gemm_skinny<1, 1, 4, YDT>), 1)
+    if (g.M <= 8) SQ_DECODE((k_gemm_skinny<1, 1, 4, YDT>), 1)
+    if (mt == 1) {
+      if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT>), 9)
+      SQ_DECODE((k_gemm_decode<4, 1, 7, YDT>), 4)
+    }
     if (mt == 2) {
       if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT>), 9)
       SQ_DECODE((k_gemm_decode<4, 2, 6, YDT>), 4)
