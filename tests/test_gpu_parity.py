@@ -96,6 +96,26 @@ def test_norm_quant_none_many_rows(dtype, k):
                      label=f"{dtype}/none/{m}x{k}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_layernorm_mean_offsets(dtype):
+    # LayerNorm statistics on both sides of the kernel's switch between the
+    # one-pass variance (sum x^2 <= 256 sum (x - mean)^2) and the centred
+    # second pass: offsets of 0..1000 spreads, and constant rows
+    k = 4096
+    g = torch.Generator().manual_seed(77)
+    base = torch.randn(12, k, generator=g)
+    offsets = torch.tensor([0.0, 1.0, 14.0, 15.0, 15.9, 16.1, 17.0, 40.0, 1000.0, 3.0e3, 0.0, 0.0])
+    x = base + offsets[:, None]
+    x[10] = 7.25                                             # constant row: variance 0
+    x[11] = -3.0e-3                                          # constant, tiny
+    x = x.to(TORCH_DT[dtype])
+    gamma, beta = params(k, 78, "layernorm")
+    xq, xs = sq.sq_norm_quant(cuda(x), "layernorm", cuda(gamma), cuda(beta), 1e-5)
+    torch.cuda.synchronize()
+    check_norm_quant(to_numpy(x), dtype, "layernorm", np_or_none(gamma), np_or_none(beta), 1e-5, host(xq), host(xs),
+                     label=f"offsets/{dtype}")
+
+
 def test_norm_quant_repeatable():
     x = cuda(rand_tokens(64, 4096, "f16", 5, n_outliers=4))
     g, b = params(4096, 6, "layernorm")

@@ -31,8 +31,9 @@ struct RawRow {
 // Statistics of a binary32 row held in registers (padding holds zeros) and the
 // normalised y in place: LayerNorm ((x - mean) * rstd) * gamma + beta, RMSNorm
 // (x * rstd) * gamma; a NULL gamma / beta means 1 / 0. Sums are taken in
-// binary64 in a fixed order (LayerNorm: two passes, centred on the binary64
-// mean) and rounded once to binary32; rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
+// binary64 in a fixed order and rounded once to binary32 (LayerNorm: the
+// variance in one pass where that is provably accurate enough, else centred on
+// the binary64 mean); rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
 template <int NORM, int NV, int THREADS>
 __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const float* __restrict__ gamma,
                                               const float* __restrict__ beta, float eps, RedRing<THREADS>& red,
@@ -40,39 +41,61 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
   const int nvec = K >> 3;
   float mu = 0.0f, r = 1.0f;
   if constexpr (NORM == SQ_NORM_LAYERNORM) {
-    // one partial sum per vector (independent dependency chains), combined in a fixed order
-    double p1[NV];
+    // One pass: S1 = sum x and S2' = sum x^2 (per-vector partial sums,
+    // independent dependency chains, combined in a fixed order), then
+    // sum (x - mean)^2 = S2' - S1 * mean. Every x^2 is exact in binary64 and
+    // the sums have at most ~24 rounding steps in a chain, so that difference
+    // is within 2^-46.7 S2' of the exact value; where S2' <= 256 sum (x - mean)^2
+    // this is 2^-38.7 relative, far inside the near-tie margin of the binary32
+    // result. Rows whose mean dominates their spread (including constant rows)
+    // take the centred second pass instead.
+    double p1[NV], q1[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      p1[i] = 0.0;
+      const double d0 = static_cast<double>(v[i][0]);
+      p1[i] = d0;
+      q1[i] = d0 * d0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p1[i] += static_cast<double>(v[i][e]);
-    }
-    double s1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) s1 += p1[i];
-    s1 = block_sum<THREADS>(s1, red.at(rk++));
-    const double mean = s1 / static_cast<double>(K);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) opaque(v[i][e]);   // convert again below rather than keep 2*8*NV doubles
-    double p2[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      p2[i] = 0.0;
-      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double d = static_cast<double>(v[i][e]) - mean;
-          p2[i] = __builtin_fma(d, d, p2[i]);
-        }
+      for (int e = 1; e < 8; ++e) {
+        const double d = static_cast<double>(v[i][e]);
+        p1[i] += d;
+        q1[i] = __builtin_fma(d, d, q1[i]);
       }
     }
-    double s2 = 0.0;
+    double s1 = 0.0, sq = 0.0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) s2 += p2[i];
-    s2 = block_sum<THREADS>(s2, red.at(rk++));
+    for (int i = 0; i < NV; ++i) {
+      s1 += p1[i];
+      sq += q1[i];
+    }
+    block_sum2<THREADS>(s1, sq, red.at(rk++));
+    const double mean = s1 / static_cast<double>(K);
+    const double cross = s1 * mean;
+    double s2;
+    if (cross <= sq * (1.0 - 1.0 / 256.0)) {                 // workgroup-uniform
+      s2 = sq - cross;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) opaque(v[i][e]);   // convert again below rather than keep 2*8*NV doubles
+      double p2[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        p2[i] = 0.0;
+        if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double d = static_cast<double>(v[i][e]) - mean;
+            p2[i] = __builtin_fma(d, d, p2[i]);
+          }
+        }
+      }
+      s2 = 0.0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) s2 += p2[i];
+      s2 = block_sum<THREADS>(s2, red.at(rk++));
+    }
     mu = static_cast<float>(mean);
     r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
   } else if constexpr (NORM == SQ_NORM_RMSNORM) {

@@ -174,7 +174,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // every thread reaches only once it has read the buffer's previous contents.
 template <int THREADS>
 struct RedRing {
-  double buf[2][THREADS / kWave];
+  double buf[2][2 * (THREADS / kWave)];                  // room for two values per wave
   __device__ __forceinline__ double* at(int k) { return buf[k & 1]; }
 };
 
@@ -188,6 +188,27 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) t += red[i];
   return t;
+}
+
+// Two sums with one barrier (same order as block_sum for each).
+template <int THREADS>
+__device__ __forceinline__ void block_sum2(double& a, double& b, double* red) {
+  constexpr int kWaves = THREADS / kWave;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (threadIdx.x % kWave == 0) {
+    red[threadIdx.x / kWave] = a;
+    red[kWaves + threadIdx.x / kWave] = b;
+  }
+  __syncthreads();
+  double ta = 0.0, tb = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    ta += red[i];
+    tb += red[kWaves + i];
+  }
+  a = ta;
+  b = tb;
 }
 
 template <int THREADS>
