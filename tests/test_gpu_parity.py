@@ -179,7 +179,9 @@ GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 
                (16, 48, 320), (32, 100, 576), (33, 17, 192), (48, 70, 4160), (63, 130, 2112), (64, 2048, 9216),
                (5, 36, 1984),
                # decode kernel, 144-channel strips (N >= 16384): ragged last strip, K tails
-               (33, 16400, 320), (20, 16384, 1088), (64, 16416, 2112), (12, 16400, 704), (9, 300, 1216)]
+               (33, 16400, 320), (20, 16384, 1088), (64, 16416, 2112), (12, 16400, 704), (9, 300, 1216),
+               # GEMV (up to 4 tokens): K tails inside a 256-byte segment, ragged N
+               (3, 130, 320), (4, 16400, 1216), (2, 77, 704), (1, 1000, 4160)]
 
 
 @pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))

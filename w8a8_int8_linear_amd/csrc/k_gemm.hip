@@ -13,8 +13,9 @@
 //    by XCD and in column groups, so tiles that share operand rows run at the
 //    same time on the same L2. k_gemm_tile_k64 is the same tile with 64-byte
 //    slices in a 4-stage ring, for K % 128 == 64.
-//  * k_gemm_skinny, k_gemm_decode -- decode shapes (M <= 64), bound by
-//    streaming wq from HBM (described at the kernels).
+//  * k_gemv (up to 4 tokens, vector ALUs) and k_gemm_decode (5..64 tokens,
+//    MFMA) -- decode shapes, bound by streaming wq from HBM (described at the
+//    kernels).
 //
 // MFMA operand order: the A operand (rows = lane % 16) carries 16 rows of wq and
 // the B operand (columns = lane % 16) 16 rows of xq, so the 16x16 result tile
@@ -454,47 +455,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   }
 }
 
-// ----------------------------------------------------------------------------- skinny kernel
+// ----------------------------------------------------------------------------- decode helpers
 
 // Decode shapes (M <= 64) are bound by streaming wq once from HBM. HBM and the
 // L2 serve a wave's load best when it covers whole 128-byte lines: a load in
 // the MFMA register layout (16 rows x 64 bytes) reaches about 2/3 of the rate
-// of one that covers 4 rows x 256 bytes. So both operands travel by
-// buffer->LDS DMA in 4-row x 256-byte blocks and are read back in the MFMA
-// layout with ds_read_b128.
-//
-// K is walked in 256-byte segments (four MFMA K steps). One segment of a
-// 16-row operand tile is four DMA blocks of 1 KiB, block i holding rows
-// 4i .. 4i+3. Inside a block, DMA lane L (LDS slot L, 16 bytes) fetches row
-// 4i + ((L >> 1) & 3), 16-byte chunk 2 (L >> 3) + (L & 1) of the segment; the
-// blocks sit kDecBlock = 1152 bytes apart. A fragment read of K step t has
-// lanes 0..31 on 16 rows x chunks 4t, 4t+1 (lanes 32..63: 4t+2, 4t+3); with
-// this placement those 32 lanes hit 32 distinct 16-byte slots of a 512-byte
-// window, so the read is bank-conflict free.
-//
-// A workgroup of four waves owns NT tiles of 16 output channels and all MT
-// token tiles. Per segment each wave issues block `wave` of every operand tile
-// (NT + MT DMA instructions), and computes K step `wave` of the segment for
-// all NT x MT output tiles; the four partial accumulators are summed through
-// LDS at the end. Segments go through an R-stage LDS ring, R - 1 in flight.
+// of one that covers 4 or 8 rows x 256 or 128 bytes, so the decode kernels
+// never load weights in the MFMA layout directly.
 constexpr int kDecWaves = 4;
-constexpr int kDecSeg = 256;                 // K bytes per segment
-constexpr int kDecBlock = 1152;              // LDS distance between the DMA blocks of one tile
-constexpr int kDecTile = 4 * kDecBlock;      // LDS bytes of one 16-row operand tile, one segment
-
-// Byte offset, inside a 16-row operand tile, fetched by DMA lane `lane` of block `blk`.
-__device__ __forceinline__ uint32_t dec_src(int lane, int blk, int K) {
-  const int row = 4 * blk + ((lane >> 1) & 3);
-  const int chunk = 2 * (lane >> 3) + (lane & 1);
-  return static_cast<uint32_t>(row * K + 16 * chunk);
-}
-
-// LDS offset, inside one operand tile, of the fragment lane `lane` reads for K step t.
-__device__ __forceinline__ int dec_frag(int lane, int t) {
-  const int r = lane & 15, c = 4 * t + (lane >> 4);
-  return kDecBlock * (r >> 2) + 16 * (8 * (c >> 1) + 2 * (r & 3) + (c & 1));
-}
-
+// Buffer-load cache policy for the decode weight stream, read exactly once:
+// non-temporal. Measured on the 1-token GEMV, N = 36864: 6.5 against 5.8 TB/s.
+constexpr int kStreamPolicy = 2;
 // s_waitcnt immediate: vmcnt(n), lgkmcnt(0), expcnt not waited on.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
@@ -534,152 +505,6 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 #pragma unroll
   for (; i < N; ++i)
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[i]) : "v"(a[i]) : "memory");
-}
-
-template <int NT, int MT, int R, int YDT>
-__global__ __launch_bounds__(64 * kDecWaves) void k_gemm_skinny(const int8_t* __restrict__ xq,
-                                                                const float* __restrict__ xs,
-                                                                const int8_t* __restrict__ wq,
-                                                                const float* __restrict__ ws,
-                                                                const float* __restrict__ bias, void* __restrict__ y,
-                                                                int M, int N, int K) {
-  static_assert(R >= 3 && R <= 8, "ring depth");
-  constexpr int kStage = (NT + MT) * kDecTile;
-  constexpr int kPerWave = NT + MT;                           // DMA instructions per wave per segment
-  static_assert(kStage >= NT * MT * 1024, "a stage holds one wave's partial accumulators");
-  // One array per stage: the compiler then knows which DMA each LDS access depends on.
-  __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
-  __shared__ __attribute__((aligned(1024))) int8_t st1[kStage];
-  __shared__ __attribute__((aligned(1024))) int8_t st2[kStage];
-  __shared__ __attribute__((aligned(1024))) int8_t st3[R > 3 ? kStage : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t st4[R > 4 ? kStage : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t st5[R > 5 ? kStage : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t st6[R > 6 ? kStage : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t st7[R > 7 ? kStage : 16];
-  auto stage = [&](auto k) -> int8_t* {
-    constexpr int i = decltype(k)::value;
-    if constexpr (i == 0) return st0;
-    else if constexpr (i == 1) return st1;
-    else if constexpr (i == 2) return st2;
-    else if constexpr (i == 3) return st3;
-    else if constexpr (i == 4) return st4;
-    else if constexpr (i == 5) return st5;
-    else if constexpr (i == 6) return st6;
-    else return st7;
-  };
-
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * (16 * NT);
-  const int rows_w = min(16 * NT, N - n0);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc_n(wq + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(rows_w * K));
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc_n(xq, static_cast<uint32_t>(M * K));
-  const uint32_t src = dec_src(lane, wid, K);
-  const int frag = dec_frag(lane, wid);
-  const int steps = K >> 6;
-  const int segs = (steps + 3) >> 2;
-
-  // Loads of a segment past the end use an offset beyond every buffer: they
-  // return zeros without touching memory, so the loop needs no branches around
-  // its loads (the compiler then keeps exact wait counts). Within the last
-  // segment, K steps past K read bytes of the next row (or zeros) and are
-  // skipped by the wave that owns them.
-  constexpr int kNowhere = 0x40000000;
-  auto issue = [&](auto k, int seg) {
-    const int so = seg < segs ? seg * kDecSeg : kNowhere;
-    int8_t* stg = stage(k);
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(stg + j * kDecTile + wid * kDecBlock), 16,
-                                               src + static_cast<uint32_t>(16 * j * K), so, 0, 0);
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stg + (NT + t) * kDecTile + wid * kDecBlock), 16,
-                                               src + static_cast<uint32_t>(16 * t * K), so, 0, 0);
-  };
-
-  v4i acc[NT][MT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[j][t] = v4i{0, 0, 0, 0};
-
-  // prologue: segments 0 .. R-2, in order (the waits count loads in issue order;
-  // the stages being distinct objects, the compiler could otherwise interleave them)
-#define SQ_DEC_PRO(I) \
-  if constexpr (I < R - 1) { issue(std::integral_constant<int, I>{}, I); memory_opaque(); }
-  SQ_DEC_PRO(0) SQ_DEC_PRO(1) SQ_DEC_PRO(2) SQ_DEC_PRO(3) SQ_DEC_PRO(4) SQ_DEC_PRO(5) SQ_DEC_PRO(6)
-#undef SQ_DEC_PRO
-
-  auto step = [&](auto k, int seg) {
-    constexpr int kk = decltype(k)::value;
-    // wait for this wave's loads of `seg`, then for everyone's DMA
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * kPerWave));
-    stage_barrier();
-    issue(std::integral_constant<int, (kk + R - 1) % R>{}, seg + R - 1);
-    if (4 * seg + wid < steps) {
-      const uint32_t base = lds_addr(stage(k)) + frag;
-      uint32_t addr[NT + MT];
-#pragma unroll
-      for (int i = 0; i < NT + MT; ++i) addr[i] = base + i * kDecTile;
-      v4i f[NT + MT];                                         // NT wq fragments, then MT xq fragments
-      lds_read_frags(f, addr);
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[j][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[j], f[NT + t], acc[j][t], 0, 0, 0);
-    }
-  };
-  // Whole rounds of R steps in the loop, the remainder after it: with no
-  // conditional step inside the loop body, no path through it skips a refill,
-  // and the explicit waits stay the only ones the compiler needs.
-  int base = 0;
-  for (; base + R <= segs; base += R) {
-#define SQ_DEC_STEP(I) \
-  if constexpr (I < R) step(std::integral_constant<int, I>{}, base + I);
-    SQ_DEC_STEP(0) SQ_DEC_STEP(1) SQ_DEC_STEP(2) SQ_DEC_STEP(3) SQ_DEC_STEP(4) SQ_DEC_STEP(5) SQ_DEC_STEP(6)
-    SQ_DEC_STEP(7)
-#undef SQ_DEC_STEP
-  }
-#define SQ_DEC_TAIL(I) \
-  if constexpr (I < R - 1) { if (base + I < segs) step(std::integral_constant<int, I>{}, base + I); }
-  SQ_DEC_TAIL(0) SQ_DEC_TAIL(1) SQ_DEC_TAIL(2) SQ_DEC_TAIL(3) SQ_DEC_TAIL(4) SQ_DEC_TAIL(5) SQ_DEC_TAIL(6)
-#undef SQ_DEC_TAIL
-
-  // sum the four waves' partials: waves 1..3 park theirs in stages 0..2
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  stage_barrier();
-  auto park = [&](int8_t* stg) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) reinterpret_cast<v4i*>(stg)[(j * MT + t) * 64 + lane] = acc[j][t];
-  };
-  if (wid == 1) park(st0);
-  else if (wid == 2) park(st1);
-  else if (wid == 3) park(st2);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  stage_barrier();
-  if (wid != 0) return;
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int i = (j * MT + t) * 64 + lane;
-      acc[j][t] += reinterpret_cast<const v4i*>(st0)[i] + reinterpret_cast<const v4i*>(st1)[i] +
-                   reinterpret_cast<const v4i*>(st2)[i];
-    }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int m = 16 * t + (lane & 15);
-    if (m >= M) continue;
-    const float xsm = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = n0 + 16 * j + 4 * (lane >> 4);
-      if (n < N) store4<YDT>(y, N, m, n, acc[j][t], xsm, ws, bias);
-    }
-  }
 }
 
 // ----------------------------------------------------------------------------- decode kernel, 128-byte segments
@@ -760,7 +585,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
       const uint32_t src = static_cast<uint32_t>(16 * tile * K) + (half ? lane_src1 : lane_src0);
       const int dst = real ? ((w ? 0 : NT) + tile) * kDec2Tile + half * 1024 : kTiles * kDec2Tile;
       if (w)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(stg + dst), 16, src, real ? so : kDecNowhere, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(stg + dst), 16, src, real ? so : kDecNowhere, 0,
+                                                 kStreamPolicy);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stg + dst), 16, src, real ? so : kDecNowhere, 0, 0);
     }
@@ -840,39 +666,141 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
   }
 }
 
+// ----------------------------------------------------------------------------- GEMV kernel (up to 8 tokens)
+
+// y[m, n] for one output, same rounding as store4.
+template <int YDT>
+__device__ __forceinline__ void store1(void* __restrict__ y, int N, int m, int n, int acc, float xs,
+                                       const float* __restrict__ ws, const float* __restrict__ bias) {
+  const int64_t off = static_cast<int64_t>(m) * N + n;
+  if constexpr (YDT == SQ_DT_I32) {
+    static_cast<int*>(y)[off] = acc;
+  } else {
+    float t = mul_rn(mul_rn(static_cast<float>(acc), xs), ws[n]);
+    if (bias) t = add_rn(t, bias[n]);
+    if constexpr (YDT == SQ_DT_F32) static_cast<float*>(y)[off] = t;
+    else static_cast<uint16_t*>(y)[off] = static_cast<uint16_t>(YDT == SQ_DT_F16 ? f32_to_f16_rne(t) : f32_to_bf16_rne(t));
+  }
+}
+
+// Decode with a handful of tokens on the vector ALUs: the weight stream is the
+// whole cost, and a load of 4 rows x 256 bytes (whole lines) per wave
+// instruction streams at the full HBM rate with no LDS staging or barriers.
+// A workgroup owns 16 channels and its four waves split K; lane l holds the
+// 16-byte K chunk l % 16 of rows 4 i + l / 16 (i = 0..3) of each 256-byte
+// segment, multiplies it against the same chunk of each token with
+// v_dot4_i32_i8 (int32 accumulation, exact), and keeps 4 x MM partial sums.
+// At the end the 16 lanes of a row are summed by DPP and the four waves
+// through LDS. Integer sums are exact, so the order does not matter.
+template <int MM, int U, int YDT>
+__global__ __launch_bounds__(256) void k_gemv(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                              const int8_t* __restrict__ wq, const float* __restrict__ ws,
+                                              const float* __restrict__ bias, void* __restrict__ y, int M, int N,
+                                              int K) {
+  __shared__ int red[kDecWaves][16][MM];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int rows_w = min(16, N - n0);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc_n(wq + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(rows_w * K));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc_n(xq, static_cast<uint32_t>(M * K));
+  const int c = lane & 15, g = lane >> 4;
+  const int segs = (K + 255) >> 8;
+  const int q = (segs + kDecWaves - 1) / kDecWaves;
+  const int s0 = wid * q, s1 = min(s0 + q, segs);
+  int acc[4][MM];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[i][m] = 0;
+
+  auto seg_step = [&](int s) {
+    // chunks past K (only in a last, partial segment) load zeros
+    const bool ok = s * 256 + 16 * c < K;
+    v4i w[4], x[MM];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rw, ok ? static_cast<uint32_t>((4 * i + g) * K + 16 * c) : kDecNowhere,
+                                         s * 256, kStreamPolicy));
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+      x[m] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rx, ok ? static_cast<uint32_t>(m * K + 16 * c) : kDecNowhere, s * 256, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][m] = __builtin_amdgcn_sdot4(w[i][j], x[m][j], acc[i][m], false);
+  };
+  int s = s0;
+  for (; s + U <= s1; s += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) seg_step(s + u);
+  }
+  for (; s < s1; ++s) seg_step(s);
+
+  // sum the 16 lanes of each row (one DPP row), then the four waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      int v = acc[i][m];
+      v += dpp_move<kDppXor1>(v);
+      v += dpp_move<kDppXor2>(v);
+      v += dpp_move<kDppHalfMirror>(v);
+      v += dpp_move<kDppMirror>(v);
+      if (c == 0) red[wid][4 * i + g][m] = v;
+    }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 16 * MM) {
+    const int row = t & 15, m = t >> 4;
+    const int n = n0 + row;
+    if (m < M && n < N) {
+      int v = 0;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) v += red[w][row][m];
+      store1<YDT>(y, N, m, n, v, (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
+    }
+  }
+}
+
 namespace {
 
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) {
-    // Up to 8 tokens: the 256-byte-segment kernel, one channel tile per
-    // workgroup. More tokens: the 128-byte-segment kernel with up to 9
-    // channel tiles per workgroup, so that each token segment serves many
-    // weight tiles (fewer at small N, to keep every CU busy). Measured on
-    // K = 9216, N = 9216 / 36864.
+    // Up to 4 tokens: the vector-ALU GEMV, 16 channels per workgroup. More:
+    // the MFMA decode kernel with up to 9 channel tiles per workgroup, so that
+    // each token segment serves many weight tiles (fewer at small N, to keep
+    // every CU busy). Measured on K = 9216, N = 9216 / 36864.
     const int mt = (g.M + 15) / 16;
     const bool wide = g.N >= 16384;
-#define SQ_DECODE(KERN, NTV)                                                                                 \
+#define SQ_DECODE(KERN, CH)                                                                                  \
   {                                                                                                          \
-    hipLaunchKernelGGL(KERN, dim3((g.N + 16 * NTV - 1) / (16 * NTV)), dim3(64 * kDecWaves), 0, st, g.xq,    \
-                       g.x_scale, g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                              \
+    hipLaunchKernelGGL(KERN, dim3((g.N + (CH) - 1) / (CH)), dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale,   \
+                       g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
     return hipGetLastError();                                                                                \
   }
-    if (g.M <= 8) SQ_DECODE((k_gemm_skinny<1, 1, 4, YDT>), 1)
+    if (g.M == 1) SQ_DECODE((k_gemv<1, 3, YDT>), 16)
+    if (g.M == 2) SQ_DECODE((k_gemv<2, 3, YDT>), 16)
+    if (g.M <= 4) SQ_DECODE((k_gemv<4, 2, YDT>), 16)
     if (mt == 1) {
-      if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT>), 9)
-      SQ_DECODE((k_gemm_decode<4, 1, 7, YDT>), 4)
+      if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT>), 144)
+      SQ_DECODE((k_gemm_decode<4, 1, 7, YDT>), 64)
     }
     if (mt == 2) {
-      if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT>), 9)
-      SQ_DECODE((k_gemm_decode<4, 2, 6, YDT>), 4)
+      if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT>), 144)
+      SQ_DECODE((k_gemm_decode<4, 2, 6, YDT>), 64)
     }
     if (mt == 3) {
-      if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT>), 9)
-      SQ_DECODE((k_gemm_decode<3, 3, 5, YDT>), 3)
+      if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT>), 144)
+      SQ_DECODE((k_gemm_decode<3, 3, 5, YDT>), 48)
     }
-    if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT>), 9)
-    SQ_DECODE((k_gemm_decode<3, 4, 5, YDT>), 3)
+    if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT>), 144)
+    SQ_DECODE((k_gemm_decode<3, 4, 5, YDT>), 48)
 #undef SQ_DECODE
   }
   const int tiles_m = (g.M + kTile - 1) / kTile;
