@@ -198,7 +198,7 @@ def test_gemm_i32_exact(mnk):
 
 def test_gemm_int32_range_at_max_k():
     k = sq.SQ_K_MAX
-    for m in [3, 70]:                                        # skinny and tiled kernels
+    for m in [3, 70]:                                        # GEMV and tiled kernels
         xq = torch.full((m, k), 127, dtype=torch.int8)
         xq[1] = -127
         wq = torch.full((5, k), 127, dtype=torch.int8)
