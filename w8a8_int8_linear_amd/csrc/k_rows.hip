@@ -24,9 +24,17 @@ struct RawRow {
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * THREADS;
       if (vi < nvec) raw_load<T>(xrow + static_cast<size_t>(vi) * 8 * Storage<T>::kBytes, r[i]);
+      else r[i] = Raw8<T>{};   // padding: zeros, never reloaded
     }
   }
 };
+
+// Stand-ins for a missing gamma (ones) or beta (zeros): read at offset 0 for
+// every vector, so one code path serves all cases. x * 1 is exact, and x + 0
+// differs from x only for -0, which leaves every code and the row maximum as
+// they are.
+static __constant__ float kOnes8[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+static __constant__ float kZeros8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 
 // Statistics of a binary32 row held in registers (padding holds zeros) and the
 // normalised y in place: LayerNorm ((x - mean) * rstd) * gamma + beta, RMSNorm
@@ -115,20 +123,21 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
     s2 = block_sum<THREADS>(s2, red.at(rk++));
     r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
   }
+  const float* gp = gamma ? gamma : kOnes8;
+  const float* bp = beta ? beta : kZeros8;
+  const int gmask = gamma ? -1 : 0, bmask = beta ? -1 : 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = threadIdx.x + i * THREADS;
     if (vi >= nvec) continue;
     float g[8], b[8];
-    if (gamma) load8_f32(gamma + 8 * vi, g);
-    if (NORM == SQ_NORM_LAYERNORM && beta) load8_f32(beta + 8 * vi, b);
+    load8_f32(gp + (8 * vi & gmask), g);
+    if constexpr (NORM == SQ_NORM_LAYERNORM) load8_f32(bp + (8 * vi & bmask), b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float t = v[i][e];
-      if constexpr (NORM == SQ_NORM_LAYERNORM) t = mul_rn(sub_rn(t, mu), r);
-      if constexpr (NORM == SQ_NORM_RMSNORM) t = mul_rn(t, r);
-      if (gamma) t = mul_rn(t, g[e]);
-      if (NORM == SQ_NORM_LAYERNORM && beta) t = add_rn(t, b[e]);
+      if constexpr (NORM == SQ_NORM_LAYERNORM) t = add_rn(mul_rn(mul_rn(sub_rn(t, mu), r), g[e]), b[e]);
+      if constexpr (NORM == SQ_NORM_RMSNORM) t = mul_rn(mul_rn(t, r), g[e]);
       v[i][e] = t;
     }
   }
@@ -297,14 +306,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
   } else {
     float v[NV][8];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
-        widen8<T>(raw.r[i], v[i]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-      }
-    }
+    for (int i = 0; i < NV; ++i) widen8<T>(raw.r[i], v[i]);   // padding vectors hold zeros
     if (refill) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
@@ -381,14 +383,7 @@ __global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ 
     raw.load(x, row, K);
     float v[NV][8];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
-        widen8<T>(raw.r[i], v[i]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-      }
-    }
+    for (int i = 0; i < NV; ++i) widen8<T>(raw.r[i], v[i]);   // padding vectors hold zeros
     normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
 #pragma unroll
     for (int i = 0; i < NV; ++i)

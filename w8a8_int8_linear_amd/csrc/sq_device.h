@@ -247,25 +247,30 @@ struct Quantizer {
   // Codes of 8 values, packed little-endian into two 32-bit words. On the
   // fast path |t| <= amax * fl32(1/step) < 127.5, so rne(t) needs no clamp;
   // the exact path clamps (a subnormal step may push the quotient past 127).
+  // One comparison covers all 8 elements: the largest |t - rne(t)|. (NaN and
+  // Inf inputs are outside the contract; such elements get some code.)
   __device__ __forceinline__ uint2 codes8(const float y[8]) const {
-    float q[8];
-    bool slow = exact_only;
+    if (zero) return make_uint2(0u, 0u);                 // workgroup-uniform
+    float q[8], d[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float t = mul_rn(y[i], rcp);
       q[i] = rintf(t);
-      slow |= !(fabsf(sub_rn(t, q[i])) < 0.499969482421875f);  // 0.5 - 2^-15
+      d[i] = sub_rn(t, q[i]);
     }
-    if (slow) {
+    float dm = fabsf(d[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) dm = fmaxf(dm, fabsf(d[i]));
+    if (exact_only || !(dm < 0.499969482421875f)) {     // 0.5 - 2^-15
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(rintf(div_rn(y[i], step)), -127.0f), 127.0f);
     }
-    uint32_t w0 = 0, w1 = 0;
+    int c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b = static_cast<uint32_t>(zero ? 0 : static_cast<int>(q[i])) & 0xffu;
-      if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
-    }
+    for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(q[i]);
+    // low bytes: perm(hi, lo, sel) picks bytes of {hi:lo}; 0x0c gives 0x00
+    const uint32_t w0 = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u) | __builtin_amdgcn_perm(c[3], c[2], 0x04000c0cu);
+    const uint32_t w1 = __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u) | __builtin_amdgcn_perm(c[7], c[6], 0x04000c0cu);
     return make_uint2(w0, w1);
   }
 };
