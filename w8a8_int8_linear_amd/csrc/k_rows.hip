@@ -285,7 +285,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(ys[i]);
+        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(ys[i]));
       }
     } else {
       // recompute x * gamma below rather than keep pass one's 8*NV products in registers
@@ -298,7 +298,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
         if (vi < nvec) {
           float y[8];
           none_y(raw, i, gv, y);
-          *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(y);
+          store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(y));
           if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
         }
       }
@@ -332,7 +332,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * THREADS;
-      if (vi < nvec) *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(vi) * 8) = qz.codes8(v[i]);
+      if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(v[i]));
     }
   }
 }
@@ -430,14 +430,13 @@ __global__ __launch_bounds__(256) void k_colmax(const void* __restrict__ w, int 
   constexpr int B = Storage<T>::kBytes;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (vi < nvec) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const char* base = static_cast<const char*>(w) + static_cast<size_t>(vi) * 8 * B;
     int64_t r = r0;
     for (; r + 8 <= r1; r += 8) {
       Raw8<T> v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(base + (r + u) * K * B);
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + (r + u) * K * B);
         v[u].a = __builtin_bit_cast(uint4, __builtin_nontemporal_load(p));
         if constexpr (B == 4) v[u].b = __builtin_bit_cast(uint4, __builtin_nontemporal_load(p + 1));
       }

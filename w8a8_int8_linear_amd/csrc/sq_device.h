@@ -53,12 +53,22 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
 template <typename T> struct Raw8 { uint4 a; };
 template <> struct Raw8<f32_t> { uint4 a, b; };
 
+// Rows are streamed once, so the loads are non-temporal (they do not displace
+// reused data from the caches).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 template <typename T> __device__ __forceinline__ void raw_load(const void* p, Raw8<T>& r) {
-  r.a = *reinterpret_cast<const uint4*>(p);
+  r.a = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
 template <> __device__ __forceinline__ void raw_load<f32_t>(const void* p, Raw8<f32_t>& r) {
-  r.a = reinterpret_cast<const uint4*>(p)[0];
-  r.b = reinterpret_cast<const uint4*>(p)[1];
+  r.a = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  r.b = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + 1));
+}
+
+// 8 int8 codes (two packed words) to p (8-byte aligned), non-temporal: the
+// codes are written once and read by a later kernel.
+__device__ __forceinline__ void store_codes8(int8_t* p, uint2 w) {
+  __builtin_nontemporal_store(u32x2_t{w.x, w.y}, reinterpret_cast<u32x2_t*>(p));
 }
 
 // Widen 8 stored elements exactly to binary32.
