@@ -42,6 +42,11 @@ def parse():
                    help="also run one plain device copy of this size (counter calibration runs)")
     p.add_argument("--summarize-counters", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="turn rocprofv3 CSV output of this benchmark into profiles/ summaries and exit")
+    p.add_argument("--decode-sweep", action="store_true",
+                   help="time the decode GEMMs (K=9216, N in {9216, 36864}, 1..64 tokens) with rotating weight "
+                        "copies and exit")
+    p.add_argument("--summarize-decode", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace of --decode-sweep into a profiles/ table and exit")
     return p.parse_args()
 
 
@@ -148,6 +153,87 @@ def summarize_counters(trace_dir, fetch_dir, write_dir):
     with open(os.path.join(ROOT, "profiles", "hbm_traffic_mtnlg530b_width.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
+
+
+# ----------------------------------------------------------------------------- decode sweep
+
+DEC_K = 9216                                  # OPT-66B hidden size
+DEC_NS = [9216, 36864]                        # the square projection and fc1
+DEC_MS = [1, 2, 4, 8, 16, 32, 48, 64]
+DEC_WARM, DEC_ITERS = 2, 12
+DEC_CMD = "rocprofv3 --kernel-trace -d <dir> -o run --output-format csv -- python3 bench.py --decode-sweep"
+
+
+def decode_bytes(m, n, k=DEC_K):
+    """Algorithmic bytes of one decode GEMM: Wq, Xq, both scale vectors and the fp16 output."""
+    return n * k + m * k + 4 * (m + n) + 2 * m * n
+
+
+def decode_sweep():
+    """Decode GEMMs at the OPT-66B width with enough weight copies (>= 600 MB) rotating that no
+    launch finds its weights in the 256 MB MALL; HIP-event medians per shape (the launch gap
+    included; the rocprofv3 trace of this run gives the kernel durations)."""
+    import torch
+    import w8a8_int8_linear_amd as sq
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    for n in DEC_NS:
+        copies = max(2, -(-600_000_000 // (n * DEC_K)))
+        ws = [torch.randint(-127, 128, (n, DEC_K), dtype=torch.int8, generator=gen).cuda() for _ in range(copies)]
+        wsc = (torch.rand(n, generator=gen) * 0.01).cuda()
+        for m in DEC_MS:
+            xq = torch.randint(-127, 128, (m, DEC_K), dtype=torch.int8, generator=gen).cuda()
+            xs = (torch.rand(m, generator=gen) * 0.01).cuda()
+            y = torch.empty(m, n, dtype=torch.float16, device="cuda")
+            for i in range(DEC_WARM):
+                sq.sq_w8a8_gemm(xq, xs, ws[i % copies], wsc, y=y, out_dtype=torch.float16)
+            torch.cuda.synchronize()
+            ts = []
+            for i in range(DEC_ITERS):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                sq.sq_w8a8_gemm(xq, xs, ws[i % copies], wsc, y=y, out_dtype=torch.float16)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            ts.sort()
+            med = ts[len(ts) // 2]
+            print(json.dumps({"decode": [m, n, DEC_K], "us_event_median": round(med, 2),
+                              "GBps": round(decode_bytes(m, n) / med / 1e3, 1)}), flush=True)
+            del xq, y
+        del ws
+        torch.cuda.empty_cache()
+
+
+def summarize_decode(trace_dir):
+    """Kernel durations of a --decode-sweep trace, matched to its shapes by dispatch order."""
+    import csv
+    import glob
+    hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    rows = [r for r in csv.DictReader(open(hits[0])) if "sq::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = DEC_WARM + DEC_ITERS
+    shapes = [(m, n) for n in DEC_NS for m in DEC_MS]
+    if len(rows) != per * len(shapes):
+        raise SystemExit(f"expected {per * len(shapes)} dispatches, found {len(rows)}")
+    lines = ["# Decode GEMM kernel durations (rocprofv3 kernel trace): OPT-66B width, K = 9216, fp16 out", "",
+             f"Command: `{DEC_CMD}`, then `python bench.py --summarize-decode <dir>`.", "",
+             "Each shape: 2 warm-up and 12 timed launches, rotating weight copies totalling >= 600 MB so that "
+             "no launch finds its weights in the MALL. Bytes = Wq + Xq + scales + fp16 output; "
+             "the bar is 75% of 8 TB/s.", "",
+             "| tokens | N | kernel | median us | min us | TB/s | 75% bar us |", "|---|---|---|---|---|---|---|"]
+    for i, (m, n) in enumerate(shapes):
+        rs = rows[i * per + DEC_WARM:(i + 1) * per]
+        du = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs)
+        med = du[len(du) // 2]
+        name = rs[0]["Kernel_Name"].split("(")[0].replace("void ", "")
+        b = decode_bytes(m, n)
+        lines.append(f"| {m} | {n} | `{name}` | {med:.2f} | {du[0]:.2f} | {b / med / 1e6:.2f} | {b / 6e6:.2f} |")
+    with open(os.path.join(ROOT, "profiles", "decode_gemm_opt66b_k9216.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 class Timer:
@@ -275,10 +361,16 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
+    if args.summarize_decode:
+        summarize_decode(args.summarize_decode)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.decode_sweep:
+        decode_sweep()
+        return
     import torch
     import w8a8_int8_linear_amd as sq
     from synth import WORKLOADS
