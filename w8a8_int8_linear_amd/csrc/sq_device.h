@@ -169,12 +169,17 @@ __device__ __forceinline__ double wave_sum(double v) {
   return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_move<kDppXor1>(v));
-  v = fmaxf(v, dpp_move<kDppXor2>(v));
-  v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_move<kDppMirror>(v));
-  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
+// Max over a wave of non-negative binary32 values, taken on their bit patterns
+// (for v >= 0 the IEEE order is the integer order), so each DPP step is a
+// single v_max_i32 with a DPP source and the last step runs on scalar units.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  int u = __float_as_int(v);
+  u = max(u, dpp_move<kDppXor1>(u));
+  u = max(u, dpp_move<kDppXor2>(u));
+  u = max(u, dpp_move<kDppHalfMirror>(u));
+  u = max(u, dpp_move<kDppMirror>(u));
+  return __int_as_float(max(max(__builtin_amdgcn_readlane(u, 0), __builtin_amdgcn_readlane(u, 16)),
+                            max(__builtin_amdgcn_readlane(u, 32), __builtin_amdgcn_readlane(u, 48))));
 }
 
 // Workgroup reductions with one barrier each: wave results go to LDS, and
@@ -222,15 +227,16 @@ __device__ __forceinline__ void block_sum2(double& a, double& b, double* red) {
 }
 
 template <int THREADS>
-__device__ __forceinline__ float block_max(float v, float* red) {
+__device__ __forceinline__ float block_max(float v, float* red) {   // v >= 0
   constexpr int kWaves = THREADS / kWave;
-  v = wave_max(v);
+  v = wave_max_nonneg(v);
   if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
-  float t = red[0];
+  const int* r = reinterpret_cast<const int*>(red);
+  int t = r[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) t = fmaxf(t, red[i]);
-  return t;
+  for (int i = 1; i < kWaves; ++i) t = max(t, r[i]);
+  return __int_as_float(t);
 }
 
 // ----------------------------------------------------------------------------- INT8 codes
