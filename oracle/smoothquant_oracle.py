@@ -40,6 +40,18 @@ R5  calibration records |y| of the fp32 activations the quantiser would see
     (the norm applied with the unfolded gamma, beta).
 R6  the GEMM epilogue is fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n]),
     plus an optional bias fl32(. + b[n]), then round-half-even to the output type.
+R7  per-tensor granularity ("SmoothQuant, in depth", "Granularity: O1, O2, O3":
+    per-tensor weights at every level, a static activation scale at O3; the
+    level table itself is lost): O2 takes one dynamic step for the whole
+    activation tensor, fl32(max |y| / 127) over every element; O3 a static step
+    fixed at calibration; per-tensor weights one step for the whole W-hat.
+    Codes follow R1, clipping included (values beyond a static step's range
+    clip, as the page's failure-mode note on static scales says). The per-row
+    and per-channel scale vectors the GEMM reads hold the step repeated, so
+    R6 is unchanged.
+R8  the static activation step is fl32(max_j fl32(a_j / s_j) / 127): the
+    smoothed input of channel j is y_j / s_j, so its calibration maximum is
+    a_j / s_j (a_j from R5, s_j from R4).
 
 Where a step rounds a real number that the oracle computes exactly (R2, R4),
 it also reports how far that number lies from the binary32 rounding boundary,
@@ -61,6 +73,7 @@ __all__ = [
     "row_stats", "normalize", "quantize_rows", "norm_quant", "norm_quant_row_variants",
     "calibrate", "weight_colmax", "smoothing_factors", "fold",
     "int_gemm", "int_gemm_loops", "dequantize", "w8a8_linear",
+    "quantize_tensor", "norm_quant_per_tensor", "static_step", "fold_per_tensor",
 ]
 
 F32 = np.float32
@@ -343,6 +356,62 @@ def fold(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=None, beta=
     return {"s": s, "s_dist": dist, "s_other": other, "w_colmax": wmax,
             "gamma_f": gamma_f.astype(F32), "beta_f": None if beta_f is None else beta_f.astype(F32),
             "wq": wq, "w_scale": w_scale, "w_hat": w_hat}
+
+
+# --------------------------------------------------------------------------- per-tensor granularities (R7, R8)
+
+def quantize_tensor(y, step=None):
+    """One INT8 step for a whole tensor (reading R7).
+
+    step None: the dynamic step fl32(max |y| / 127) over every element (O2, and
+    per-tensor weights); otherwise the given static step (O3). Codes are
+    clip(round_half_even(fl32(y / step)), -127, 127); a step that is not
+    positive gives all-zero codes. Returns (codes int8, step fp32 scalar).
+    """
+    y = np.atleast_2d(np.asarray(y, dtype=F32))
+    if step is None:
+        amax = np.max(np.abs(y)) if y.size else F32(0)
+        step = F32(amax) / F32(QMAX)
+    step = F32(step)
+    if not step > 0:
+        return np.zeros(y.shape, np.int8), step
+    q = np.clip(np.rint(y / step), -QMAX, QMAX)
+    return q.astype(np.int8), step
+
+
+def norm_quant_per_tensor(x, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5, step=None):
+    """Norm with the folded gamma', beta' (exactly as norm_quant), then one step for the tensor.
+
+    step None: per-tensor dynamic (O2); a number: the static calibrated step (O3).
+    Returns (codes int8 [M,K], x_scale fp32 [M] = the step repeated, info) with
+    info["near_tie"] as in norm_quant.
+    """
+    x32 = widen(x, dtype)
+    if norm == NONE:
+        y = normalize(x32, NONE, gamma=gamma_f)
+        info = {"near_tie": np.zeros(x32.shape[0], bool), "alt": {}}
+    else:
+        mu, var, tie, alt = _stats_block(x32, norm)
+        y = normalize(x32, norm, mu, var, gamma_f, beta_f, eps)
+        info = {"mu": mu, "var": var, "near_tie": tie, "alt": alt}
+    q, st = quantize_tensor(y, step)
+    info["y"] = y
+    return q, np.full(x32.shape[0], st, F32), info
+
+
+def static_step(act_absmax, s):
+    """Static per-tensor activation step from calibration (reading R8): fl32(max_j fl32(a_j / s_j) / 127)."""
+    r = np.asarray(act_absmax, F32) / np.asarray(s, F32)
+    return F32(np.max(r) if r.size else F32(0)) / F32(QMAX)
+
+
+def fold_per_tensor(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=None, beta=None, s=None):
+    """fold() with one weight step for the whole W-hat (reading R7): w_scale holds it repeated."""
+    f = fold(act_absmax, w, dtype, alpha, eps, norm, gamma, beta, s)
+    wq, st = quantize_tensor(f["w_hat"])
+    f["wq"] = wq
+    f["w_scale"] = np.full(f["w_hat"].shape[0], st, F32)
+    return f
 
 
 # --------------------------------------------------------------------------- O4 GEMM and epilogue
