@@ -147,6 +147,69 @@ sq_status sq_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* bias, void* y, sq_dtype y_dt,
                        int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * Per-tensor granularities ("SmoothQuant, in depth", section "Granularity: O1,
+ * O2, O3 and what kernels run today": every level uses per-tensor weight
+ * scales, the fastest (O3) a static activation scale, the most accurate (O1)
+ * the finest; the level table itself did not survive, so O1 = per-token
+ * dynamic, O2 = per-tensor dynamic, O3 = per-tensor static is a reading). A
+ * per-tensor step is still returned as a full scale vector, the step repeated,
+ * so sq_w8a8_gemm consumes every granularity unchanged.
+ */
+
+/*
+ * Norm + quantisation with one dynamic step for the whole tensor.
+ *   Arguments as sq_norm_quant. y is computed exactly as there.
+ *   xq       [M, K] int8 out: codes of y with step = fl32(max_{m,j} |y[m, j]| / 127).
+ *   x_scale  [M] fp32 out: the step in every entry (also used as the buffer of
+ *            the row maxima while the call runs).
+ * Two passes over x (the rows' maxima, then the codes) with one small
+ * reduction between them.
+ */
+sq_status sq_norm_quant_per_tensor(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                   sq_norm norm, const float* gamma_f, const float* beta_f, float eps,
+                                   int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Norm + quantisation with a static step fixed at calibration ("SmoothQuant,
+ * in depth", section on failure modes: a static scale clips inputs outside the
+ * calibrated range).
+ *   Arguments as sq_norm_quant, plus
+ *   step     [1] fp32 device pointer: the step (from sq_static_step, or any
+ *            value the caller chose); a step <= 0 gives all-zero codes.
+ *   xq       [M, K] int8 out: clip(round_half_even(fl32(y / step)), -127, 127).
+ *   x_scale  [M] fp32 out: *step in every entry (must not alias step).
+ */
+sq_status sq_norm_quant_static(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                               sq_norm norm, const float* gamma_f, const float* beta_f, float eps,
+                               const float* step, int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * The static activation step from calibration: the smoothed input of channel j
+ * is y_j / s_j ("LLM.int8() and SmoothQuant", section "going deeper": X-hat =
+ * X diag(s)^-1), so its calibration maximum is a_j / s_j.
+ *   act_absmax [K] fp32 from smoothquant_calibrate (UNFOLDED norm output).
+ *   s          [K] fp32 from smoothquant_fold (or its per-tensor variant).
+ *   step       [1] fp32 out: fl32(max_j fl32(act_absmax[j] / s[j]) / 127).
+ *   K as for the other calls.
+ */
+sq_status sq_static_step(const float* act_absmax, const float* s, int64_t K, float* step, void* stream);
+
+/*
+ * smoothquant_fold with one weight step for the whole W-hat (the per-tensor
+ * weights of O1-O3). Arguments and the outputs s_out, gamma_out, beta_out as
+ * smoothquant_fold; then
+ *   wq       [N, K] int8: codes of W-hat = fl32(W * s) with step
+ *            fl32(max_{n,j} |W-hat[n, j]| / 127);
+ *   w_scale  [N] fp32: that step in every entry (also the buffer of the row
+ *            maxima while the call runs).
+ */
+sq_status smoothquant_fold_per_tensor(const float* act_absmax, const void* w, sq_dtype w_dt,
+                                      int64_t N, int64_t K, double alpha, float eps,
+                                      sq_norm norm, const float* gamma, const float* beta,
+                                      float* s_out, float* gamma_out, float* beta_out,
+                                      int8_t* wq, float* w_scale, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* sq_status_string(sq_status s);
 

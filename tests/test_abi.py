@@ -20,9 +20,10 @@ def _declared():
     return set(re.findall(r"^(?:sq_status|const char\*)\s+(\w+)\s*\(", text, re.M))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     assert _declared() == {"smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
-                           "sq_status_string"}
+                           "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step",
+                           "smoothquant_fold_per_tensor", "sq_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -56,7 +57,33 @@ def fold(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=Non
     return L.smoothquant_fold(a, w, dt, n, k, ctypes.c_double(alpha), F(eps), norm, g, b, s, go, bo, wq, ws, None)
 
 
+def nqt(x=A, dt=1, m=16, k=512, norm=0, g=None, b=None, eps=1e-5, xq=A, xs=A):
+    return L.sq_norm_quant_per_tensor(x, dt, m, k, norm, g, b, F(eps), xq, xs, None)
+
+
+def nqs(x=A, dt=1, m=16, k=512, norm=0, g=None, b=None, eps=1e-5, step=A, xq=A, xs=A):
+    return L.sq_norm_quant_static(x, dt, m, k, norm, g, b, F(eps), step, xq, xs, None)
+
+
+def sstep(a=A, s=A, k=512, step=A):
+    return L.sq_static_step(a, s, k, step, None)
+
+
+def foldt(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=None, s=A, go=A, bo=None,
+          wq=A, ws=A):
+    return L.smoothquant_fold_per_tensor(a, w, dt, n, k, ctypes.c_double(alpha), F(eps), norm, g, b, s, go, bo, wq,
+                                         ws, None)
+
+
 @pytest.mark.parametrize("call,code", [
+    (lambda: nqt(x=None), 1), (lambda: nqt(xs=None), 1), (lambda: nqt(dt=3), 2), (lambda: nqt(k=100), 3),
+    (lambda: nqt(xq=A4), 4), (lambda: nqt(norm=0, b=A), 5), (lambda: nqt(norm=1, eps=0.0), 5),
+    (lambda: nqs(step=None), 1), (lambda: nqs(x=None), 1), (lambda: nqs(dt=7), 2), (lambda: nqs(m=0), 3),
+    (lambda: nqs(step=ctypes.c_void_p((1 << 20) + 2)), 4), (lambda: nqs(norm=2, b=A), 5),
+    (lambda: sstep(a=None), 1), (lambda: sstep(s=None), 1), (lambda: sstep(step=None), 1), (lambda: sstep(k=0), 3),
+    (lambda: sstep(k=100), 3), (lambda: sstep(step=ctypes.c_void_p((1 << 20) + 2)), 4),
+    (lambda: foldt(a=None), 1), (lambda: foldt(ws=None), 1), (lambda: foldt(dt=3), 2), (lambda: foldt(n=0), 3),
+    (lambda: foldt(alpha=1.5), 5), (lambda: foldt(w=A4), 4),
     (lambda: nq(x=None), 1), (lambda: nq(xq=None), 1), (lambda: nq(xs=None), 1),
     (lambda: nq(dt=3), 2), (lambda: nq(dt=7), 2),
     (lambda: nq(m=0), 3), (lambda: nq(k=0), 3), (lambda: nq(k=100), 3), (lambda: nq(k=133184), 3),

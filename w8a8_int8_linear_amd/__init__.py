@@ -18,7 +18,11 @@ from ._lib import (  # noqa: F401
     lib,
     smoothquant_calibrate,
     smoothquant_fold,
+    smoothquant_fold_per_tensor,
     sq_norm_quant,
+    sq_norm_quant_per_tensor,
+    sq_norm_quant_static,
+    sq_static_step,
     sq_w8a8_gemm,
     status_string,
 )

@@ -24,7 +24,9 @@ _DT = {torch.float32: SQ_DT_F32, torch.float16: SQ_DT_F16, torch.bfloat16: SQ_DT
 _NORM = {"none": SQ_NORM_NONE, "layernorm": SQ_NORM_LAYERNORM, "rmsnorm": SQ_NORM_RMSNORM,
          SQ_NORM_NONE: SQ_NORM_NONE, SQ_NORM_LAYERNORM: SQ_NORM_LAYERNORM, SQ_NORM_RMSNORM: SQ_NORM_RMSNORM}
 
-EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm", "sq_status_string")
+EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
+           "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step", "smoothquant_fold_per_tensor",
+           "sq_status_string")
 
 
 class SmoothQuantError(RuntimeError):
@@ -42,6 +44,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smoothquant_fold.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
     lib.sq_norm_quant.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P]
     lib.sq_w8a8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.sq_norm_quant_per_tensor.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P]
+    lib.sq_norm_quant_static.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P]
+    lib.sq_static_step.argtypes = [P, P, I64, P, P]
+    lib.smoothquant_fold_per_tensor.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
     lib.sq_status_string.argtypes = [I]
     lib.sq_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -102,10 +108,19 @@ def smoothquant_calibrate(x, norm="none", gamma=None, beta=None, eps=1e-5, absma
 
 
 def smoothquant_fold(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, beta=None, out=None):
-    """Smoothing factors, folded norm parameters and INT8 weights for w [N, K].
+    """Smoothing factors, folded norm parameters and INT8 weights for w [N, K] (one step per output row).
 
     Returns dict(s, gamma_f, beta_f, wq, w_scale); `out` may supply those buffers.
     """
+    return _fold("smoothquant_fold", act_absmax, w, alpha, eps, norm, gamma, beta, out)
+
+
+def smoothquant_fold_per_tensor(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, beta=None, out=None):
+    """As smoothquant_fold with one weight step for the whole tensor (w_scale holds it repeated)."""
+    return _fold("smoothquant_fold_per_tensor", act_absmax, w, alpha, eps, norm, gamma, beta, out)
+
+
+def _fold(fn, act_absmax, w, alpha, eps, norm, gamma, beta, out):
     _dev(w, "w", _ACT)
     n, k = w.shape
     _dev(act_absmax, "act_absmax", torch.float32, (k,))
@@ -125,7 +140,7 @@ def smoothquant_fold(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, be
                          ("beta_f", (k,), torch.float32), ("wq", (n, k), torch.int8), ("w_scale", (n,), torch.float32)]:
         _dev(out[key], key, dt, shp)
     with torch.cuda.device(dev):
-        _check("smoothquant_fold", lib.smoothquant_fold(
+        _check(fn, getattr(lib, fn)(
             _ptr(act_absmax), _ptr(w), _DT[w.dtype], n, k, float(alpha), eps, _NORM[norm], _ptr(gamma), _ptr(beta),
             _ptr(out["s"]), _ptr(out["gamma_f"]), _ptr(out["beta_f"]), _ptr(out["wq"]), _ptr(out["w_scale"]),
             _stream(w)))
@@ -134,6 +149,34 @@ def smoothquant_fold(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, be
 
 def sq_norm_quant(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
     """Fused norm (folded gamma', beta') + per-token INT8: returns (xq [M, K] int8, x_scale [M] fp32)."""
+    return _nq("sq_norm_quant", x, norm, gamma_f, beta_f, eps, xq, x_scale)
+
+
+def sq_norm_quant_per_tensor(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
+    """Fused norm + INT8 with one dynamic step for the whole tensor (x_scale holds it repeated)."""
+    return _nq("sq_norm_quant_per_tensor", x, norm, gamma_f, beta_f, eps, xq, x_scale)
+
+
+def sq_norm_quant_static(x, step, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
+    """Fused norm + INT8 with a static step (a [1] fp32 device tensor), codes clipped to +-127."""
+    _dev(step, "step", torch.float32, (1,))
+    return _nq("sq_norm_quant_static", x, norm, gamma_f, beta_f, eps, xq, x_scale, step)
+
+
+def sq_static_step(act_absmax, s, step=None):
+    """Static activation step fl32(max_j fl32(a_j / s_j) / 127) into a [1] fp32 tensor."""
+    k = act_absmax.shape[0]
+    _dev(act_absmax, "act_absmax", torch.float32, (k,))
+    _dev(s, "s", torch.float32, (k,))
+    if step is None:
+        step = torch.empty(1, dtype=torch.float32, device=s.device)
+    _dev(step, "step", torch.float32, (1,))
+    with torch.cuda.device(s.device):
+        _check("sq_static_step", lib.sq_static_step(_ptr(act_absmax), _ptr(s), k, _ptr(step), _stream(s)))
+    return step
+
+
+def _nq(fn, x, norm, gamma_f, beta_f, eps, xq, x_scale, *step):
     _dev(x, "x", _ACT)
     m, k = x.shape
     _dev(gamma_f, "gamma_f", torch.float32, (k,))
@@ -145,9 +188,9 @@ def sq_norm_quant(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, 
     _dev(xq, "xq", torch.int8, (m, k))
     _dev(x_scale, "x_scale", torch.float32, (m,))
     with torch.cuda.device(x.device):
-        _check("sq_norm_quant", lib.sq_norm_quant(
-            _ptr(x), _DT[x.dtype], m, k, _NORM[norm], _ptr(gamma_f), _ptr(beta_f), eps, _ptr(xq), _ptr(x_scale),
-            _stream(x)))
+        _check(fn, getattr(lib, fn)(
+            _ptr(x), _DT[x.dtype], m, k, _NORM[norm], _ptr(gamma_f), _ptr(beta_f), eps, *[_ptr(t) for t in step],
+            _ptr(xq), _ptr(x_scale), _stream(x)))
     return xq, x_scale
 
 

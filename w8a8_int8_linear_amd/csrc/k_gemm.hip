@@ -89,7 +89,6 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n
 
 constexpr int kTile = 256;                     // output tile edge (m and n)
 constexpr int kSlice = 64;                     // K bytes per LDS stage: one MFMA K step
-constexpr int kStages = 4;                     // LDS ring depth: slices in flight = kStages - 1
 constexpr int kStageBytes = kTile * kSlice;    // one operand, one stage: 16 KiB
 constexpr int kDmaPerWave = kStageBytes / 1024 / 8;   // 1 KiB DMA instructions per wave per operand: 2
 
@@ -185,7 +184,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_k64(const int8_t* __restri
                                                       const int8_t* __restrict__ wq, const float* __restrict__ ws,
                                                       const float* __restrict__ bias, void* __restrict__ y,
                                                       int M, int N, int K, int tiles_m, int tiles_n, int group) {
-  // Ring of kStages stages per operand, each its own array: the compiler then
+  // Ring of four stages per operand, each its own array: the compiler then
   // sees that a DMA into one stage never aliases the fragment reads of another
   // and inserts no wait of its own before those reads.
   __shared__ __attribute__((aligned(1024))) int8_t lA0[kStageBytes];

@@ -1,365 +1,10 @@
-// Row-streaming kernels: fused norm + per-token INT8 quantisation, calibration
+// Row-streaming kernels: fused norm + per-token quantisation, calibration
 // absmax, and the offline fold (weight column maxima, smoothing factors; the
-// weight codes are the NONE-norm quantiser run over W with gamma = s).
-//
-// The quantiser keeps a whole row in registers between its statistics, its
-// normalisation and its codes, so each element is read from HBM once and its
-// code written once. Workgroups stride over rows and load the next row while
-// they work on the current one, which hides HBM latency even when only one
-// workgroup fits on a CU (a 20480-wide binary32 row is 80 KiB of registers).
-#include "sq_device.h"
-#include "sq_launch.h"
-#include "smoothquant.h"
+// weight codes are the NONE-norm quantiser run over W with gamma = s). The
+// building blocks they share with the per-tensor passes are in rows.h.
+#include "rows.h"
 
 namespace sq {
-
-// A row held as raw 16-byte vectors: thread t owns vectors t, t + THREADS, ...
-template <typename T, int NV, int THREADS>
-struct RawRow {
-  Raw8<T> r[NV];
-  __device__ __forceinline__ void load(const void* x, int64_t row, int K) {
-    const char* xrow = static_cast<const char*>(x) + row * K * Storage<T>::kBytes;
-    const int nvec = K >> 3;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int vi = threadIdx.x + i * THREADS;
-      if (vi < nvec) raw_load<T>(xrow + static_cast<size_t>(vi) * 8 * Storage<T>::kBytes, r[i]);
-      else r[i] = Raw8<T>{};   // padding: zeros, never reloaded
-    }
-  }
-};
-
-// Stand-ins for a missing gamma (ones) or beta (zeros): read at offset 0 for
-// every vector, so one code path serves all cases. x * 1 is exact, and x + 0
-// differs from x only for -0, which leaves every code and the row maximum as
-// they are.
-static __constant__ float kOnes8[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
-static __constant__ float kZeros8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-
-// Statistics of a binary32 row held in registers (padding holds zeros) and the
-// normalised y in place: LayerNorm ((x - mean) * rstd) * gamma + beta, RMSNorm
-// (x * rstd) * gamma; a NULL gamma / beta means 1 / 0. Sums are taken in
-// binary64 in a fixed order and rounded once to binary32 (LayerNorm: the
-// variance in one pass where that is provably accurate enough, else centred on
-// the binary64 mean); rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
-template <int NORM, int NV, int THREADS>
-__device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const float* __restrict__ gamma,
-                                              const float* __restrict__ beta, float eps, RedRing<THREADS>& red,
-                                              int& rk) {
-  const int nvec = K >> 3;
-  float mu = 0.0f, r = 1.0f;
-  if constexpr (NORM == SQ_NORM_LAYERNORM) {
-    // One pass: S1 = sum x and S2' = sum x^2 (per-vector partial sums,
-    // independent dependency chains, combined in a fixed order), then
-    // sum (x - mean)^2 = S2' - S1 * mean. Every x^2 is exact in binary64 and
-    // the sums have at most ~24 rounding steps in a chain, so that difference
-    // is within 2^-46.7 S2' of the exact value; where S2' <= 256 sum (x - mean)^2
-    // this is 2^-38.7 relative, far inside the near-tie margin of the binary32
-    // result. Rows whose mean dominates their spread (including constant rows)
-    // take the centred second pass instead.
-    double p1[NV], q1[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const double d0 = static_cast<double>(v[i][0]);
-      p1[i] = d0;
-      q1[i] = d0 * d0;
-#pragma unroll
-      for (int e = 1; e < 8; ++e) {
-        const double d = static_cast<double>(v[i][e]);
-        p1[i] += d;
-        q1[i] = __builtin_fma(d, d, q1[i]);
-      }
-    }
-    double s1 = 0.0, sq = 0.0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      s1 += p1[i];
-      sq += q1[i];
-    }
-    block_sum2<THREADS>(s1, sq, red.at(rk++));
-    const double mean = s1 / static_cast<double>(K);
-    const double cross = s1 * mean;
-    double s2;
-    if (cross <= sq * (1.0 - 1.0 / 256.0)) {                 // workgroup-uniform
-      s2 = sq - cross;
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) opaque(v[i][e]);   // convert again below rather than keep 2*8*NV doubles
-      double p2[NV];
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        p2[i] = 0.0;
-        if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double d = static_cast<double>(v[i][e]) - mean;
-            p2[i] = __builtin_fma(d, d, p2[i]);
-          }
-        }
-      }
-      s2 = 0.0;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) s2 += p2[i];
-      s2 = block_sum<THREADS>(s2, red.at(rk++));
-    }
-    mu = static_cast<float>(mean);
-    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
-  } else if constexpr (NORM == SQ_NORM_RMSNORM) {
-    double p2[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      p2[i] = 0.0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double d = static_cast<double>(v[i][e]);
-        p2[i] = __builtin_fma(d, d, p2[i]);
-      }
-    }
-    double s2 = 0.0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) s2 += p2[i];
-    s2 = block_sum<THREADS>(s2, red.at(rk++));
-    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
-  }
-  const float* gp = gamma ? gamma : kOnes8;
-  const float* bp = beta ? beta : kZeros8;
-  const int gmask = gamma ? -1 : 0, bmask = beta ? -1 : 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int vi = threadIdx.x + i * THREADS;
-    if (vi >= nvec) continue;
-    float g[8], b[8];
-    load8_f32(gp + (8 * vi & gmask), g);
-    if constexpr (NORM == SQ_NORM_LAYERNORM) load8_f32(bp + (8 * vi & bmask), b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float t = v[i][e];
-      if constexpr (NORM == SQ_NORM_LAYERNORM) t = add_rn(mul_rn(mul_rn(sub_rn(t, mu), r), g[e]), b[e]);
-      if constexpr (NORM == SQ_NORM_RMSNORM) t = mul_rn(mul_rn(t, r), g[e]);
-      v[i][e] = t;
-    }
-  }
-}
-
-// The per-column factors of the thread's own columns (vectors t, t + THREADS,
-// ...), kept for the workgroup's lifetime: a row quantiser reads them for
-// every element of every row, twice, which from L2 costs four times the HBM
-// bytes of a 16-bit row. Vectors [0, GREG) stay in registers, [GREG, GREG +
-// GLDS) in LDS (each thread reads back only what it wrote, so no barrier is
-// involved), the rest are re-read from memory.
-template <int NV, int THREADS, int GREG, int GLDS>
-struct ColVec {
-  static_assert(GREG + GLDS <= NV, "column vector split");
-  float r[GREG > 0 ? GREG : 1][8];
-  float4* lds;                                  // [GLDS][2][THREADS]
-  const float* __restrict__ g;
-  __device__ __forceinline__ void init(const float* __restrict__ gamma, int nvec, float4* lds_mem) {
-    g = gamma;
-    lds = lds_mem;
-    if (!gamma) return;
-#pragma unroll
-    for (int i = 0; i < GREG + GLDS; ++i) {
-      const int vi = threadIdx.x + i * THREADS;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (vi < nvec) load8_f32(gamma + 8 * vi, v);
-      if (i < GREG) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[i < GREG ? i : 0][e] = v[e];
-      } else {
-        lds[(2 * (i - GREG)) * THREADS + threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
-        lds[(2 * (i - GREG) + 1) * THREADS + threadIdx.x] = make_float4(v[4], v[5], v[6], v[7]);
-      }
-    }
-  }
-  // factors of vector i (a compile-time index after unrolling)
-  __device__ __forceinline__ void get(int i, float v[8]) const {
-    if (i < GREG) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = r[i < GREG ? i : 0][e];
-    } else if (i < GREG + GLDS) {
-      const float4 a = lds[(2 * (i - GREG)) * THREADS + threadIdx.x];
-      const float4 b = lds[(2 * (i - GREG) + 1) * THREADS + threadIdx.x];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-      load8_f32(g + 8 * (threadIdx.x + i * THREADS), v);
-    }
-  }
-};
-
-// Split of the column factors for a row layout: as many vectors in registers
-// as fit beside the raw row within 128 VGPRs (two 512-thread or one
-// 1024-thread workgroup per CU; the rest of the quantiser takes about
-// 48 + NV), then LDS up to the workgroup's share (32 / 64 / 128 KiB for
-// 256 / 512 / 1024 threads), then memory.
-template <typename T, int NV, int THREADS>
-struct ColSplit {
-  // the wide NONE layout (512 threads, more than 6 vectors each) runs one
-  // workgroup per CU: 256 VGPRs per thread and 144 KiB of LDS
-  static constexpr bool kWide = THREADS == 512 && NV > 6;
-  static constexpr int kBudget = kWide ? 256 : 128;
-  static constexpr int kRaw = NV * 2 * Storage<T>::kBytes;
-  static constexpr int kFree = (kBudget - kRaw - 48 - NV) / 8;
-  static constexpr int kReg = kFree < 0 ? 0 : (kFree < NV ? kFree : NV);
-  static constexpr int kLdsCap =
-      (kWide ? 147456 : THREADS >= 1024 ? 131072 : THREADS >= 512 ? 65536 : 32768) / (THREADS * 32);
-  static constexpr int kLds = NV - kReg < kLdsCap ? NV - kReg : kLdsCap;
-};
-
-// y of vector i of a raw row for the NONE norm: x, or fl32(x * gamma).
-template <typename T, int NV, int THREADS, int GREG, int GLDS>
-__device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
-                                       const ColVec<NV, THREADS, GREG, GLDS>& gv, float y[8]) {
-  widen8<T>(raw.r[i], y);
-  if (gv.g) {
-    float g[8];
-    gv.get(i, g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = mul_rn(y[e], g[e]);
-  }
-}
-
-// Quantise one row held raw in registers, write its codes and step, and refill
-// the raw buffer with row `next` (if next < M) as soon as each part of it is
-// free, so the next row's loads overlap this row's work within one buffer.
-//  NONE: two passes over the row (the max of |x * gamma|, then the codes).
-//        Narrow rows keep the binary32 products and refill the whole buffer
-//        before the reduction; wide rows recompute the product in pass two
-//        and refill vector i right after its codes are written.
-//  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
-//        normalise in place, then max and codes.
-template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
-__device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
-                                             int64_t row, int64_t next, int M, int K,
-                                             const float* __restrict__ gamma,
-                                             const ColVec<NV, THREADS, GREG, GLDS>& gv,
-                                             const float* __restrict__ beta, float eps, int8_t* __restrict__ xq,
-                                             float* __restrict__ x_scale, RedRing<THREADS>& red, int& rk) {
-  const int nvec = K >> 3;
-  constexpr int B = Storage<T>::kBytes;
-  int8_t* qrow = xq + row * K;
-  const bool refill = next < M;
-  // Address of the next row, formed unconditionally and used only when
-  // refill holds. (Written as refill ? next : row, ROCm 7.2's compiler turns
-  // the select into an s_cselect on a stale SCC -- the 64-bit compare went to
-  // VCC -- and reloads the current row.)
-  const char* nrow = static_cast<const char*>(x) + next * K * B;
-  if constexpr (NORM == SQ_NORM_NONE) {
-    // Narrow rows at up to 512 threads keep pass one's products for pass two
-    // (8 NV VGPRs, within the 128 of two workgroups per CU) and refill the raw
-    // buffer before the reduction; wider ones recompute x * gamma in pass two.
-    constexpr bool kKeepY = THREADS <= 512 && Storage<T>::kBytes == 2 && NV <= 5;
-    float ys[kKeepY ? NV : 1][8];
-    float pm[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      pm[i] = 0.0f;
-      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
-        float y[8];
-        none_y(raw, i, gv, y);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pm[i] = fmaxf(pm[i], fabsf(y[e]));
-          if constexpr (kKeepY) ys[i][e] = y[e];
-        }
-      }
-    }
-    if constexpr (kKeepY) {
-      if (refill) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int vi = threadIdx.x + i * THREADS;
-          if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
-        }
-      }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
-    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
-    const float step = int8_step(amax);
-    if (threadIdx.x == 0) x_scale[row] = step;
-    const Quantizer qz(step);
-    if constexpr (kKeepY) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(ys[i]));
-      }
-    } else {
-      // recompute x * gamma below rather than keep pass one's 8*NV products in registers
-#pragma unroll
-      for (int i = 0; i < NV; ++i) opaque(raw.r[i].a);
-      memory_opaque();
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) {
-          float y[8];
-          none_y(raw, i, gv, y);
-          store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(y));
-          if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
-        }
-      }
-    }
-  } else {
-    float v[NV][8];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) widen8<T>(raw.r[i], v[i]);   // padding vectors hold zeros
-    if (refill) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
-      }
-    }
-    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
-    float pm[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      pm[i] = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pm[i] = fmaxf(pm[i], fabsf(v[i][e]));
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
-    amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
-    const float step = int8_step(amax);
-    if (threadIdx.x == 0) x_scale[row] = step;
-    const Quantizer qz(step);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int vi = threadIdx.x + i * THREADS;
-      if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(v[i]));
-    }
-  }
-}
-
-// Fused norm + per-token quantisation. Workgroup b handles rows b, b + G, ...
-// (G = gridDim.x <= M); one raw row buffer, refilled with the next row while
-// the current one is being processed.
-template <typename T, int NORM, int NV, int THREADS>
-__global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__ x, int M, int K,
-                                                        const float* __restrict__ gamma,
-                                                        const float* __restrict__ beta, float eps,
-                                                        int8_t* __restrict__ xq, float* __restrict__ x_scale) {
-  __shared__ RedRing<THREADS> red;
-  // NONE keeps its column factors for the workgroup's lifetime (the norms read
-  // gamma / beta once per row)
-  constexpr int kReg = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kReg : 0;
-  constexpr int kLds = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kLds : 0;
-  __shared__ float4 gl[kLds > 0 ? 2 * kLds * THREADS : 1];
-  ColVec<NV, THREADS, kReg, kLds> gv;
-  const int64_t G = gridDim.x;
-  RawRow<T, NV, THREADS> raw;
-  raw.load(x, blockIdx.x, K);
-  gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
-  int rk = 0;
-  for (int64_t row = blockIdx.x; row < M; row += G)
-    quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk);
-}
 
 // Calibration with a norm: workgroups stride over rows, normalise each with the
 // unfolded gamma / beta, keep the per-column max of |y| in registers and merge
@@ -372,7 +17,6 @@ __global__ __launch_bounds__(THREADS) void k_calibrate(const void* __restrict__ 
   __shared__ RedRing<THREADS> red;
   __shared__ float4 gl[2 * THREADS];                       // 8 floats per thread: the merge transpose
   int rk = 0;
-  const int nvec = K >> 3;
   float cm[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
@@ -493,44 +137,6 @@ __global__ void k_scales(const float* __restrict__ act_absmax, float* __restrict
 
 namespace {
 
-struct RowCfg { int threads, nv; };
-
-// Smallest (threads, vectors per thread) covering K/8 vectors of the row. The
-// NONE quantiser of 16-bit rows of 65544 .. 81920 columns takes 512 threads x
-// 20 vectors instead of 1024 x 10: one workgroup per CU then holds all of its
-// column factors (13 vectors in registers, 7 in LDS) where the 1024-thread
-// layout has room for 7 of 10.
-RowCfg row_cfg(int K, int norm, int bytes) {
-  const int nvec = K >> 3;
-  if (norm == SQ_NORM_NONE && bytes == 2 && nvec > 8192 && nvec <= 10240) return {512, 20};
-  static const RowCfg table[] = {{256, 1}, {256, 2}, {256, 3}, {256, 4}, {512, 3},  {512, 4},   {512, 5},
-                                 {512, 6}, {1024, 4}, {1024, 6}, {1024, 8}, {1024, 10}, {1024, 13}, {1024, 17}};
-  for (const RowCfg& c : table)
-    if (c.threads * c.nv >= nvec) return c;
-  return {1024, 17};
-}
-
-// Workgroups that fit on the device at once (all CUs x the kernel's occupancy).
-hipError_t resident_blocks(const void* kernel, int threads, int* out) {
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
-  *out = (e == hipSuccess) ? cus * (per_cu > 0 ? per_cu : 1) : 0;
-  return e;
-}
-
-template <typename T, int NORM, int NV, int THREADS>
-hipError_t launch_nq(const RowArgs& a, hipStream_t st) {
-  auto kern = k_norm_quant<T, NORM, NV, THREADS>;
-  int cap = 0;
-  if (hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), THREADS, &cap)) return e;
-  const int grid = static_cast<int>(a.rows < cap ? a.rows : cap);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, st, a.x, static_cast<int>(a.rows), a.K, a.gamma, a.beta,
-                     a.eps, a.xq, a.x_scale);
-  return hipGetLastError();
-}
-
 template <typename T, int NORM, int NV, int THREADS>
 hipError_t launch_cal(const RowArgs& a, hipStream_t st) {
   // enough rows per workgroup to keep the atomic merges few, enough workgroups to fill the device
@@ -572,26 +178,21 @@ hipError_t launch_colmax_dt(sq_dtype dt, const void* x, int64_t N, int K, float*
   }
 }
 
-template <bool CAL, typename T, int NORM, int NV, int THREADS>
-hipError_t dispatch_one(const RowArgs& a, hipStream_t st) {
-  if constexpr (CAL) return launch_cal<T, NORM, NV, THREADS>(a, st);
-  else return launch_nq<T, NORM, NV, THREADS>(a, st);
-}
+template <bool CAL, typename T, int NORM>
+struct RowLaunch {
+  const RowArgs& a;
+  hipStream_t st;
+  template <int NV, int THREADS>
+  hipError_t run() const {
+    if constexpr (CAL) return launch_cal<T, NORM, NV, THREADS>(a, st);
+    else return launch_nq<T, NORM, NV, THREADS, false>(a, nullptr, 0, st);
+  }
+};
 
 template <bool CAL, typename T, int NORM>
 hipError_t dispatch_cfg(const RowArgs& a, hipStream_t st) {
-  const RowCfg c = row_cfg(a.K, NORM, Storage<T>::kBytes);
-  if constexpr (!CAL && NORM == SQ_NORM_NONE && Storage<T>::kBytes == 2) {
-    if (c.threads == 512 && c.nv == 20) return dispatch_one<CAL, T, NORM, 20, 512>(a, st);
-  }
-#define SQ_ROW_CASE(TH, NVV) \
-  if (c.threads == TH && c.nv == NVV) return dispatch_one<CAL, T, NORM, NVV, TH>(a, st);
-  SQ_ROW_CASE(256, 1) SQ_ROW_CASE(256, 2) SQ_ROW_CASE(256, 3) SQ_ROW_CASE(256, 4)
-  SQ_ROW_CASE(512, 3) SQ_ROW_CASE(512, 4) SQ_ROW_CASE(512, 5) SQ_ROW_CASE(512, 6)
-  SQ_ROW_CASE(1024, 4) SQ_ROW_CASE(1024, 6) SQ_ROW_CASE(1024, 8) SQ_ROW_CASE(1024, 10)
-  SQ_ROW_CASE(1024, 13) SQ_ROW_CASE(1024, 17)
-#undef SQ_ROW_CASE
-  return hipErrorInvalidValue;
+  constexpr bool kWide = !CAL && NORM == SQ_NORM_NONE && Storage<T>::kBytes == 2;
+  return with_row_cfg<kWide>(a.K, NORM, Storage<T>::kBytes, RowLaunch<CAL, T, NORM>{a, st});
 }
 
 template <bool CAL, typename T>

@@ -1,0 +1,91 @@
+// Per-tensor steps ("SmoothQuant, in depth", section "Granularity: O1, O2, O3
+// and what kernels run today": per-tensor weight scales at every level, and a
+// static activation scale at the fastest one; its section on failure modes:
+// a static scale clips inputs outside the calibrated range).
+//
+//  * Per-tensor dynamic: a first row pass writes each row's max |y| into the
+//    scale vector, one workgroup reduces those to the tensor's step and writes
+//    it into every entry, and a second row pass writes the codes with it.
+//  * Per-tensor static: one row pass with a step from calibration,
+//    fl32(max_j fl32(a_j / s_j) / 127) (k_static_step), codes clipped.
+// The scale vectors the GEMM reads then hold the one step repeated, so the
+// GEMM and its epilogue are the same as for per-token / per-channel steps.
+#include "rows.h"
+
+namespace sq {
+
+// scale[0 .. n) holds non-negative row maxima; replace every entry with the
+// tensor's step fl32(max / 127). One workgroup: every read precedes the
+// barrier inside the block maximum, every write follows it.
+__global__ __launch_bounds__(1024) void k_tensor_step(float* __restrict__ scale, int64_t n) {
+  __shared__ float red[1024 / 64];
+  int m = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) m = max(m, __float_as_int(scale[i]));
+  const float step = int8_step(block_max<1024>(__int_as_float(m), red));
+  for (int64_t i = threadIdx.x; i < n; i += 1024) scale[i] = step;
+}
+
+// step[0] = fl32(max_j fl32(a_j / s_j) / 127): the smoothed input of channel j
+// is y_j / s_j, so a_j / s_j is its calibration maximum (a_j >= 0, s_j > 0).
+__global__ __launch_bounds__(1024) void k_static_step(const float* __restrict__ act_absmax,
+                                                      const float* __restrict__ s, int K, float* __restrict__ step) {
+  __shared__ float red[1024 / 64];
+  float m = 0.0f;
+  for (int j = threadIdx.x; j < K; j += 1024) m = fmaxf(m, div_rn(act_absmax[j], s[j]));
+  m = block_max<1024>(m, red);
+  if (threadIdx.x == 0) step[0] = int8_step(m);
+}
+
+namespace {
+
+template <typename T, int NORM>
+struct TensorLaunch {
+  const RowArgs& a;
+  const float* step;
+  int flags;
+  hipStream_t st;
+  template <int NV, int THREADS>
+  hipError_t run() const { return launch_nq<T, NORM, NV, THREADS, true>(a, step, flags, st); }
+};
+
+template <typename T>
+hipError_t tensor_rows(const RowArgs& a, const float* step, int flags, hipStream_t st) {
+  constexpr int B = Storage<T>::kBytes;
+  switch (a.norm) {
+    case SQ_NORM_NONE: return with_row_cfg<B == 2>(a.K, SQ_NORM_NONE, B, TensorLaunch<T, SQ_NORM_NONE>{a, step, flags, st});
+    case SQ_NORM_LAYERNORM:
+      return with_row_cfg<false>(a.K, SQ_NORM_LAYERNORM, B, TensorLaunch<T, SQ_NORM_LAYERNORM>{a, step, flags, st});
+    case SQ_NORM_RMSNORM:
+      return with_row_cfg<false>(a.K, SQ_NORM_RMSNORM, B, TensorLaunch<T, SQ_NORM_RMSNORM>{a, step, flags, st});
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t tensor_rows_dt(const RowArgs& a, const float* step, int flags, hipStream_t st) {
+  switch (a.dtype) {
+    case SQ_DT_F32: return tensor_rows<f32_t>(a, step, flags, st);
+    case SQ_DT_F16: return tensor_rows<f16_t>(a, step, flags, st);
+    case SQ_DT_BF16: return tensor_rows<bf16_t>(a, step, flags, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_norm_quant_per_tensor(const RowArgs& a, hipStream_t st) {
+  if (hipError_t e = tensor_rows_dt(a, nullptr, kRowsAmaxOnly, st)) return e;   // x_scale[m] = max |y[m, :]|
+  hipLaunchKernelGGL(k_tensor_step, dim3(1), dim3(1024), 0, st, a.x_scale, a.rows);
+  if (hipError_t e = hipGetLastError()) return e;                               // x_scale[m] = the step
+  return tensor_rows_dt(a, a.x_scale, 0, st);
+}
+
+hipError_t launch_norm_quant_given_step(const RowArgs& a, const float* step, hipStream_t st) {
+  return tensor_rows_dt(a, step, kRowsWriteScale, st);
+}
+
+hipError_t launch_static_step(const float* act_absmax, const float* s, int K, float* step, hipStream_t st) {
+  hipLaunchKernelGGL(k_static_step, dim3(1), dim3(1024), 0, st, act_absmax, s, K, step);
+  return hipGetLastError();
+}
+
+}  // namespace sq

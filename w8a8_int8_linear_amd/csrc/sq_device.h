@@ -260,11 +260,14 @@ struct Quantizer {
     exact_only = st < 0x1p-100f;
     rcp = zero ? 0.0f : div_rn(1.0f, st);
   }
-  // Codes of 8 values, packed little-endian into two 32-bit words. On the
-  // fast path |t| <= amax * fl32(1/step) < 127.5, so rne(t) needs no clamp;
-  // the exact path clamps (a subnormal step may push the quotient past 127).
-  // One comparison covers all 8 elements: the largest |t - rne(t)|. (NaN and
-  // Inf inputs are outside the contract; such elements get some code.)
+  // Codes of 8 values, packed little-endian into two 32-bit words. With the
+  // row's own step |t| <= amax * fl32(1/step) < 127.5 on the fast path, so
+  // rne(t) needs no clamp; CLIP (a step given for a whole tensor, which values
+  // may exceed) clamps it. The exact path always clamps (a subnormal step may
+  // push the quotient past 127). One comparison covers all 8 elements: the
+  // largest |t - rne(t)|. (NaN and Inf inputs are outside the contract; such
+  // elements get some code.)
+  template <bool CLIP = false>
   __device__ __forceinline__ uint2 codes8(const float y[8]) const {
     if (zero) return make_uint2(0u, 0u);                 // workgroup-uniform
     float q[8], d[8];
@@ -280,6 +283,9 @@ struct Quantizer {
     if (exact_only || !(dm < 0.499969482421875f)) {     // 0.5 - 2^-15
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(rintf(div_rn(y[i], step)), -127.0f), 127.0f);
+    } else if constexpr (CLIP) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -127.0f), 127.0f);
     }
     int c[8];
 #pragma unroll

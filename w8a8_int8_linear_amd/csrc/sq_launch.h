@@ -54,5 +54,12 @@ hipError_t launch_calibrate(const RowArgs& a, hipStream_t st);
 // norm_quant pass over W with gamma = s).
 hipError_t launch_fold_colmax_scales(const FoldArgs& f, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// One step for the whole tensor: the rows' maxima, their max, then the codes;
+// x_scale ends holding the step in every entry.
+hipError_t launch_norm_quant_per_tensor(const RowArgs& a, hipStream_t st);
+// Codes with the step *step (device), clipped; x_scale[m] = *step.
+hipError_t launch_norm_quant_given_step(const RowArgs& a, const float* step, hipStream_t st);
+// *step = fl32(max_j fl32(act_absmax[j] / s[j]) / 127).
+hipError_t launch_static_step(const float* act_absmax, const float* s, int K, float* step, hipStream_t st);
 
 }  // namespace sq

@@ -79,6 +79,13 @@ sq_status check_norm_quant(const void* x, sq_dtype x_dt, int64_t M, int64_t K, s
   return SQ_OK;
 }
 
+sq_status check_static_step(const float* act_absmax, const float* s, int64_t K, const float* step) {
+  if (!act_absmax || !s || !step) return SQ_ERR_NULL_POINTER;
+  if (sq_status st = check_k(K)) return st;
+  if (!aligned(act_absmax, 4) || !aligned(s, 4) || !aligned(step, 4)) return SQ_ERR_MISALIGNED;
+  return SQ_OK;
+}
+
 sq_status check_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
                      const float* bias, const void* y, sq_dtype y_dt, int64_t M, int64_t N, int64_t K) {
   if (!xq || !wq || !y) return SQ_ERR_NULL_POINTER;

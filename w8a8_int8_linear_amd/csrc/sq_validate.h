@@ -21,6 +21,9 @@ sq_status check_norm_quant(const void* x, sq_dtype x_dt, int64_t M, int64_t K, s
                            const float* gamma_f, const float* beta_f, float eps,
                            const int8_t* xq, const float* x_scale);
 
+// The static activation step from calibration maxima and smoothing factors.
+sq_status check_static_step(const float* act_absmax, const float* s, int64_t K, const float* step);
+
 sq_status check_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
                      const float* bias, const void* y, sq_dtype y_dt, int64_t M, int64_t N, int64_t K);
 
