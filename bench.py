@@ -47,6 +47,11 @@ def parse():
                         "copies and exit")
     p.add_argument("--summarize-decode", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace of --decode-sweep into a profiles/ table and exit")
+    p.add_argument("--granularities", action="store_true",
+                   help="time per-token, per-tensor dynamic and static activation steps and both weight-step "
+                        "folds on the default workload's sites, and exit")
+    p.add_argument("--summarize-granularities", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace --stats of --granularities into a profiles/ table and exit")
     return p.parse_args()
 
 
@@ -236,6 +241,85 @@ def summarize_decode(trace_dir):
     print("\n".join(lines))
 
 
+# ----------------------------------------------------------------------------- granularities
+
+GRAN_CMD = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+            "python3 bench.py --granularities")
+
+
+def granularity_sweep(args):
+    """Per-token vs per-tensor dynamic vs static activation steps (and per-channel vs per-tensor weight
+    steps in the fold) on the MT-NLG-width sites, HIP-event medians over 20 launches (fold: 5)."""
+    import torch
+    import w8a8_int8_linear_amd as sq
+    from synth import WORKLOADS
+    wl = WORKLOADS[5]
+    sites = build_sites(torch, sq, wl, wl.m[0])
+
+    def med(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    for d in sites:
+        m, k, n, norm = d["m"], d["k"], d["n"], d["norm"]
+        amax = sq.smoothquant_calibrate(d["x_cal"], norm, d["gamma"], d["beta"], EPS)
+        fo = sq.smoothquant_fold(amax, d["w"], wl.alpha, EPS, norm, d["gamma"], d["beta"])
+        stp = sq.sq_static_step(amax, fo["s"])
+        g, b = fo["gamma_f"], fo["beta_f"]
+        e = d["x"].element_size()
+        nq_bytes = m * k * e + m * k + 4 * m + 4 * k * (2 if b is not None else 1)
+        runs = [("per-token", lambda: sq.sq_norm_quant(d["x"], norm, g, b, EPS, d["xq"], d["xs"])),
+                ("per-tensor dynamic (2 passes)",
+                 lambda: sq.sq_norm_quant_per_tensor(d["x"], norm, g, b, EPS, d["xq"], d["xs"])),
+                ("per-tensor static", lambda: sq.sq_norm_quant_static(d["x"], stp, norm, g, b, EPS, d["xq"], d["xs"]))]
+        for name, fn in runs:
+            ms = med(fn, 20)
+            print(json.dumps({"stage": "norm_quant", "granularity": name, "site": d["site"].name, "shape": [m, k],
+                              "ms": round(ms, 4), "GBps": round(nq_bytes / ms / 1e6, 1)}), flush=True)
+        fold_bytes = 2 * n * k * e + n * k + 4 * n + 16 * k
+        for name, fn in [("per-channel", lambda: sq.smoothquant_fold(amax, d["w"], wl.alpha, EPS, norm, d["gamma"],
+                                                                      d["beta"], out=d["fold"])),
+                         ("per-tensor (3 weight passes)",
+                          lambda: sq.smoothquant_fold_per_tensor(amax, d["w"], wl.alpha, EPS, norm, d["gamma"],
+                                                                 d["beta"], out=d["fold"]))]:
+            ms = med(fn, 5)
+            print(json.dumps({"stage": "fold", "granularity": name, "site": d["site"].name, "shape": [n, k],
+                              "ms": round(ms, 4), "GBps": round(fold_bytes / ms / 1e6, 1)}), flush=True)
+
+
+def summarize_granularities(trace_dir):
+    """Kernel statistics of a --granularities run as a profiles/ table."""
+    import csv
+    import glob
+    hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no kernel stats under {trace_dir}")
+    lines = ["# rocprofv3 kernel statistics: activation and weight step granularities, MT-NLG-530B-width sites", "",
+             f"Command: `{GRAN_CMD}`, then `python bench.py --summarize-granularities <dir>`.", "",
+             "Sites: LayerNorm 8192x20480 -> fc1 and NONE 8192x81920 -> fc2 (fp16). `k_norm_quant<..., true>` is a "
+             "per-tensor pass (row maxima, or codes with a given step); `k_tensor_step` reduces the row maxima.", "",
+             "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(hits[0])):
+        if "sq::" in r["Name"]:
+            short = r["Name"].split("(")[0].replace("void ", "")
+            lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                         f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} |")
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_granularities_mtnlg530b.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 class Timer:
     """HIP events on the stream the library launches on, one pair per launch."""
 
@@ -364,12 +448,18 @@ def main():
     if args.summarize_decode:
         summarize_decode(args.summarize_decode)
         return
+    if args.summarize_granularities:
+        summarize_granularities(args.summarize_granularities)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.decode_sweep:
         decode_sweep()
+        return
+    if args.granularities:
+        granularity_sweep(args)
         return
     import torch
     import w8a8_int8_linear_amd as sq

@@ -185,7 +185,7 @@ struct RowLaunch {
   template <int NV, int THREADS>
   hipError_t run() const {
     if constexpr (CAL) return launch_cal<T, NORM, NV, THREADS>(a, st);
-    else return launch_nq<T, NORM, NV, THREADS, false>(a, nullptr, 0, st);
+    else return launch_nq<T, NORM, NV, THREADS, kRowsPerRow>(a, nullptr, 0, st);
   }
 };
 

@@ -36,51 +36,12 @@ __global__ __launch_bounds__(1024) void k_static_step(const float* __restrict__ 
   if (threadIdx.x == 0) step[0] = int8_step(m);
 }
 
-namespace {
-
-template <typename T, int NORM>
-struct TensorLaunch {
-  const RowArgs& a;
-  const float* step;
-  int flags;
-  hipStream_t st;
-  template <int NV, int THREADS>
-  hipError_t run() const { return launch_nq<T, NORM, NV, THREADS, true>(a, step, flags, st); }
-};
-
-template <typename T>
-hipError_t tensor_rows(const RowArgs& a, const float* step, int flags, hipStream_t st) {
-  constexpr int B = Storage<T>::kBytes;
-  switch (a.norm) {
-    case SQ_NORM_NONE: return with_row_cfg<B == 2>(a.K, SQ_NORM_NONE, B, TensorLaunch<T, SQ_NORM_NONE>{a, step, flags, st});
-    case SQ_NORM_LAYERNORM:
-      return with_row_cfg<false>(a.K, SQ_NORM_LAYERNORM, B, TensorLaunch<T, SQ_NORM_LAYERNORM>{a, step, flags, st});
-    case SQ_NORM_RMSNORM:
-      return with_row_cfg<false>(a.K, SQ_NORM_RMSNORM, B, TensorLaunch<T, SQ_NORM_RMSNORM>{a, step, flags, st});
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t tensor_rows_dt(const RowArgs& a, const float* step, int flags, hipStream_t st) {
-  switch (a.dtype) {
-    case SQ_DT_F32: return tensor_rows<f32_t>(a, step, flags, st);
-    case SQ_DT_F16: return tensor_rows<f16_t>(a, step, flags, st);
-    case SQ_DT_BF16: return tensor_rows<bf16_t>(a, step, flags, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
 
 hipError_t launch_norm_quant_per_tensor(const RowArgs& a, hipStream_t st) {
-  if (hipError_t e = tensor_rows_dt(a, nullptr, kRowsAmaxOnly, st)) return e;   // x_scale[m] = max |y[m, :]|
+  if (hipError_t e = ModeLaunch<kRowsAmax>::run(a, nullptr, 0, st)) return e;   // x_scale[m] = max |y[m, :]|
   hipLaunchKernelGGL(k_tensor_step, dim3(1), dim3(1024), 0, st, a.x_scale, a.rows);
   if (hipError_t e = hipGetLastError()) return e;                               // x_scale[m] = the step
-  return tensor_rows_dt(a, a.x_scale, 0, st);
-}
-
-hipError_t launch_norm_quant_given_step(const RowArgs& a, const float* step, hipStream_t st) {
-  return tensor_rows_dt(a, step, kRowsWriteScale, st);
+  return launch_rows_given_step(a, a.x_scale, false, st);                       // codes; x_scale as it is
 }
 
 hipError_t launch_static_step(const float* act_absmax, const float* s, int K, float* step, hipStream_t st) {

@@ -341,16 +341,18 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
   }
 }
 
-// Flags of the per-tensor row pass.
-constexpr int kRowsAmaxOnly = 1;     // write the row's max |y| into x_scale[row]; no codes
-constexpr int kRowsWriteScale = 2;   // with a given step: also write x_scale[row] = step
+// Modes of the fused norm + quantise kernel.
+constexpr int kRowsPerRow = 0;       // one step per row (per-token activations, per-channel weights)
+constexpr int kRowsAmax = 1;         // per-tensor first pass: each row's max |y| into x_scale[row]; no codes
+constexpr int kRowsGivenStep = 2;    // per-tensor codes with a step given for the whole tensor, clipped
 
-// One row of a per-tensor pass: either the row's max |y| alone (the first pass
-// of a per-tensor dynamic step), or the codes of y with a step given for the
-// whole tensor (the second pass, or a static calibrated step), clipped to
-// [-127, 127]. NONE then needs a single pass over the row: each vector's
-// codes are written and its raw buffer refilled with the next row at once.
-template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
+// One row of a per-tensor pass: MODE kRowsAmax writes the row's max |y| alone
+// (the first pass of a per-tensor dynamic step); kRowsGivenStep writes the
+// codes of y with a step given for the whole tensor (the second pass, or a
+// static calibrated step), clipped to [-127, 127], and x_scale[row] = step if
+// write_scale. Either way NONE needs a single pass over the row: each vector's
+// raw buffer is refilled with the next row as soon as it has been read.
+template <int MODE, typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
 __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
                                                     int64_t row, int64_t next, int M, int K,
                                                     const float* __restrict__ gamma,
@@ -358,27 +360,41 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
                                                     const float* __restrict__ beta, float eps,
                                                     int8_t* __restrict__ xq, float* __restrict__ x_scale,
                                                     RedRing<THREADS>& red, int& rk, const Quantizer& qz,
-                                                    int flags) {
+                                                    bool write_scale) {
   const int nvec = K >> 3;
   constexpr int B = Storage<T>::kBytes;
   int8_t* qrow = xq + row * K;
   const bool refill = next < M;
   const char* nrow = static_cast<const char*>(x) + next * K * B;   // used only when refill holds
-  const bool amax_only = (flags & kRowsAmaxOnly) != 0;             // uniform
+  constexpr bool amax_only = MODE == kRowsAmax;
   float amax = 0.0f;
   if constexpr (NORM == SQ_NORM_NONE) {
-    if (amax_only) {
-      float pm[NV];
+    // Where each vector is refilled right after it is read, wait for the whole
+    // row once first: otherwise the compiler, unable to tell the vectors'
+    // pending loads apart across the per-vector branches, drains every
+    // outstanding load (this row's refills included) before each vector.
+    constexpr bool kKeepY = THREADS <= 512 && Storage<T>::kBytes == 2 && NV <= 5;
+    if constexpr (amax_only || !kKeepY) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if constexpr (amax_only) {
+      // one running max, and each vector's raw buffer refilled as soon as it is read
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        pm[i] = 0.0f;
-        if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
+        const int vi = threadIdx.x + i * THREADS;
+        if (vi < nvec) {
           float y[8];
           none_y(raw, i, gv, y);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pm[i] = fmaxf(pm[i], fabsf(y[e]));
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+          if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
         }
       }
+    } else if constexpr (kKeepY) {
+      // short rows: y of the whole row in registers, the next row requested
+      // at once, then the codes (the next row's loads overlap the stores)
+      float ys[NV][8];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) none_y(raw, i, gv, ys[i]);
       if (refill) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -387,7 +403,10 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
         }
       }
 #pragma unroll
-      for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
+      for (int i = 0; i < NV; ++i) {
+        const int vi = threadIdx.x + i * THREADS;
+        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8<true>(ys[i]));
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
@@ -412,7 +431,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
       }
     }
     normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
-    if (amax_only) {
+    if constexpr (amax_only) {
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -425,10 +444,10 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
       }
     }
   }
-  if (amax_only) {
+  if constexpr (amax_only) {
     amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
     if (threadIdx.x == 0) x_scale[row] = amax;
-  } else if ((flags & kRowsWriteScale) && threadIdx.x == 0) {
+  } else if (write_scale && threadIdx.x == 0) {
     x_scale[row] = qz.step;
   }
 }
@@ -436,12 +455,12 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
 // Fused norm + per-token quantisation. Workgroup b handles rows b, b + G, ...
 // (G = gridDim.x <= M); one raw row buffer, refilled with the next row while
 // the current one is being processed.
-template <typename T, int NORM, int NV, int THREADS, bool TENSOR = false>
+template <typename T, int NORM, int NV, int THREADS, int MODE = kRowsPerRow>
 __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__ x, int M, int K,
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, float eps,
                                                         int8_t* __restrict__ xq, float* __restrict__ x_scale,
-                                                        const float* __restrict__ step_ptr, int flags) {
+                                                        const float* __restrict__ step_ptr, int write_scale) {
   __shared__ RedRing<THREADS> red;
   // NONE keeps its column factors for the workgroup's lifetime (the norms read
   // gamma / beta once per row)
@@ -454,12 +473,12 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
   raw.load(x, blockIdx.x, K);
   gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
   int rk = 0;
-  if constexpr (TENSOR) {
-    // per-tensor passes (step_ptr and flags are used only here)
-    const Quantizer qz((flags & kRowsAmaxOnly) ? 0.0f : *step_ptr);
+  if constexpr (MODE != kRowsPerRow) {
+    // per-tensor passes (step_ptr and write_scale are used only here)
+    const Quantizer qz(MODE == kRowsGivenStep ? *step_ptr : 0.0f);
     for (int64_t row = blockIdx.x; row < M; row += G)
-      quantize_row_tensor<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red,
-                                                rk, qz, flags);
+      quantize_row_tensor<MODE, T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale,
+                                                      red, rk, qz, write_scale != 0);
   } else {
     for (int64_t row = blockIdx.x; row < M; row += G)
       quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk);
@@ -515,15 +534,51 @@ hipError_t with_row_cfg(int K, int norm, int bytes, const F& f) {
 }
 
 // Fused norm + quantisation launch: one workgroup per row up to what fits on the device at once.
-template <typename T, int NORM, int NV, int THREADS, bool TENSOR>
-hipError_t launch_nq(const RowArgs& a, const float* step_ptr, int flags, hipStream_t st) {
-  auto kern = k_norm_quant<T, NORM, NV, THREADS, TENSOR>;
+template <typename T, int NORM, int NV, int THREADS, int MODE>
+hipError_t launch_nq(const RowArgs& a, const float* step_ptr, int write_scale, hipStream_t st) {
+  auto kern = k_norm_quant<T, NORM, NV, THREADS, MODE>;
   int cap = 0;
   if (hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), THREADS, &cap)) return e;
   const int grid = static_cast<int>(a.rows < cap ? a.rows : cap);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, st, a.x, static_cast<int>(a.rows), a.K, a.gamma, a.beta,
-                     a.eps, a.xq, a.x_scale, step_ptr, flags);
+                     a.eps, a.xq, a.x_scale, step_ptr, write_scale);
   return hipGetLastError();
 }
+
+
+// Launch the MODE pass of the fused kernel for a's dtype, norm and row layout.
+template <int MODE>
+struct ModeLaunch {
+  template <typename T, int NORM>
+  struct L {
+    const RowArgs& a;
+    const float* step;
+    int write_scale;
+    hipStream_t st;
+    template <int NV, int THREADS>
+    hipError_t run() const { return launch_nq<T, NORM, NV, THREADS, MODE>(a, step, write_scale, st); }
+  };
+  template <typename T>
+  static hipError_t norm(const RowArgs& a, const float* step, int write_scale, hipStream_t st) {
+    constexpr int B = Storage<T>::kBytes;
+    switch (a.norm) {
+      case SQ_NORM_NONE:
+        return with_row_cfg<B == 2>(a.K, SQ_NORM_NONE, B, L<T, SQ_NORM_NONE>{a, step, write_scale, st});
+      case SQ_NORM_LAYERNORM:
+        return with_row_cfg<false>(a.K, SQ_NORM_LAYERNORM, B, L<T, SQ_NORM_LAYERNORM>{a, step, write_scale, st});
+      case SQ_NORM_RMSNORM:
+        return with_row_cfg<false>(a.K, SQ_NORM_RMSNORM, B, L<T, SQ_NORM_RMSNORM>{a, step, write_scale, st});
+    }
+    return hipErrorInvalidValue;
+  }
+  static hipError_t run(const RowArgs& a, const float* step, int write_scale, hipStream_t st) {
+    switch (a.dtype) {
+      case SQ_DT_F32: return norm<f32_t>(a, step, write_scale, st);
+      case SQ_DT_F16: return norm<f16_t>(a, step, write_scale, st);
+      case SQ_DT_BF16: return norm<bf16_t>(a, step, write_scale, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+};
 
 }  // namespace sq

@@ -59,6 +59,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_norm_quant_per_tensor(const RowArgs& a, hipStream_t st);
 // Codes with the step *step (device), clipped; x_scale[m] = *step.
 hipError_t launch_norm_quant_given_step(const RowArgs& a, const float* step, hipStream_t st);
+// As above; x_scale is written only if write_scale (it may then be the step's own buffer).
+hipError_t launch_rows_given_step(const RowArgs& a, const float* step, bool write_scale, hipStream_t st);
 // *step = fl32(max_j fl32(act_absmax[j] / s[j]) / 127).
 hipError_t launch_static_step(const float* act_absmax, const float* s, int K, float* step, hipStream_t st);
 
