@@ -307,8 +307,11 @@ def summarize_granularities(trace_dir):
         raise SystemExit(f"no kernel stats under {trace_dir}")
     lines = ["# rocprofv3 kernel statistics: activation and weight step granularities, MT-NLG-530B-width sites", "",
              f"Command: `{GRAN_CMD}`, then `python bench.py --summarize-granularities <dir>`.", "",
-             "Sites: LayerNorm 8192x20480 -> fc1 and NONE 8192x81920 -> fc2 (fp16). `k_norm_quant<..., true>` is a "
-             "per-tensor pass (row maxima, or codes with a given step); `k_tensor_step` reduces the row maxima.", "",
+             "Sites: LayerNorm 8192x20480 -> fc1 and NONE 8192x81920 -> fc2 (fp16), folds of their weights "
+             "(81920x20480, 20480x81920). The last template argument of `k_norm_quant` is its mode: 0 one step per "
+             "row, 1 the rows' maxima (first per-tensor pass), 2 codes with a step given for the whole tensor "
+             "(second per-tensor pass, or a static step); `k_tensor_step` reduces the rows' maxima to the tensor "
+             "step.", "",
              "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(hits[0])):
         if "sq::" in r["Name"]:

@@ -40,7 +40,7 @@ R5  calibration records |y| of the fp32 activations the quantiser would see
     (the norm applied with the unfolded gamma, beta).
 R6  the GEMM epilogue is fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n]),
     plus an optional bias fl32(. + b[n]), then round-half-even to the output type.
-R7  per-tensor granularity ("SmoothQuant, in depth", "Granularity: O1, O2, O3":
+R14 per-tensor granularity ("SmoothQuant, in depth", "Granularity: O1, O2, O3":
     per-tensor weights at every level, a static activation scale at O3; the
     level table itself is lost): O2 takes one dynamic step for the whole
     activation tensor, fl32(max |y| / 127) over every element; O3 a static step
@@ -49,7 +49,7 @@ R7  per-tensor granularity ("SmoothQuant, in depth", "Granularity: O1, O2, O3":
     clip, as the page's failure-mode note on static scales says). The per-row
     and per-channel scale vectors the GEMM reads hold the step repeated, so
     R6 is unchanged.
-R8  the static activation step is fl32(max_j fl32(a_j / s_j) / 127): the
+R15 the static activation step is fl32(max_j fl32(a_j / s_j) / 127): the
     smoothed input of channel j is y_j / s_j, so its calibration maximum is
     a_j / s_j (a_j from R5, s_j from R4).
 
@@ -358,10 +358,10 @@ def fold(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=None, beta=
             "wq": wq, "w_scale": w_scale, "w_hat": w_hat}
 
 
-# --------------------------------------------------------------------------- per-tensor granularities (R7, R8)
+# --------------------------------------------------------------------------- per-tensor granularities (R14, R15)
 
 def quantize_tensor(y, step=None):
-    """One INT8 step for a whole tensor (reading R7).
+    """One INT8 step for a whole tensor (reading R14).
 
     step None: the dynamic step fl32(max |y| / 127) over every element (O2, and
     per-tensor weights); otherwise the given static step (O3). Codes are
@@ -400,13 +400,13 @@ def norm_quant_per_tensor(x, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5, s
 
 
 def static_step(act_absmax, s):
-    """Static per-tensor activation step from calibration (reading R8): fl32(max_j fl32(a_j / s_j) / 127)."""
+    """Static per-tensor activation step from calibration (reading R15): fl32(max_j fl32(a_j / s_j) / 127)."""
     r = np.asarray(act_absmax, F32) / np.asarray(s, F32)
     return F32(np.max(r) if r.size else F32(0)) / F32(QMAX)
 
 
 def fold_per_tensor(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=None, beta=None, s=None):
-    """fold() with one weight step for the whole W-hat (reading R7): w_scale holds it repeated."""
+    """fold() with one weight step for the whole W-hat (reading R14): w_scale holds it repeated."""
     f = fold(act_absmax, w, dtype, alpha, eps, norm, gamma, beta, s)
     wq, st = quantize_tensor(f["w_hat"])
     f["wq"] = wq
