@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--granularities", action="store_true",
                    help="time per-token, per-tensor dynamic and static activation steps and both weight-step "
                         "folds on the default workload's sites, and exit")
+    p.add_argument("--accuracy", action="store_true",
+                   help="synthetic accuracy study: plain INT8 vs SmoothQuant over alpha, on every workload, and exit")
+    p.add_argument("--accuracy-tokens", type=int, default=256, help="token rows per site in the accuracy study")
     p.add_argument("--summarize-granularities", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --granularities into a profiles/ table and exit")
     return p.parse_args()
@@ -323,6 +326,83 @@ def summarize_granularities(trace_dir):
     print("\n".join(lines))
 
 
+# ----------------------------------------------------------------------------- accuracy study
+
+ALPHAS = (0.5, 0.65, 0.8, 0.9)
+
+
+def reference_linear(torch, x, norm, gamma, beta, w, eps=EPS):
+    """The unquantised layer in binary64: norm(x) (unfolded gamma, beta) times W^T."""
+    x = x.double()
+    if norm == "layernorm":
+        mu = x.mean(dim=1, keepdim=True)
+        var = ((x - mu) ** 2).mean(dim=1, keepdim=True)
+        y = (x - mu) / torch.sqrt(var + eps) * gamma.double() + beta.double()
+    elif norm == "rmsnorm":
+        y = x / torch.sqrt((x * x).mean(dim=1, keepdim=True) + eps) * gamma.double()
+    else:
+        y = x
+    return y @ w.double().t()
+
+
+def ordinary_span(xq, outliers):
+    """Median over tokens of the largest |code| among the non-outlier channels: how many of the
+    127 positive levels the ordinary channels of a token actually reach."""
+    import torch
+    keep = torch.ones(xq.shape[1], dtype=torch.bool, device=xq.device)
+    keep[torch.as_tensor(outliers, dtype=torch.long, device=xq.device)] = False
+    return int(xq[:, keep].abs().amax(dim=1).median().item())
+
+
+def accuracy_site(torch, sq, wl, si, m_tokens):
+    """One site: relative output error and ordinary-channel span for each scheme."""
+    from synth import site_inputs
+    inp = site_inputs(wl.id, si, m=m_tokens, device="cuda")
+    site = wl.sites[si]
+    x, xc, w, g, b, norm = inp["x"], inp["x_cal"], inp["w"], inp["gamma"], inp["beta"], site.norm
+    y_ref = reference_linear(torch, x, norm, g, b, w)
+    ref_norm = torch.linalg.norm(y_ref).item()
+    amax = sq.smoothquant_calibrate(xc, norm, g, b, EPS)
+    wmax = sq.smoothquant_calibrate(w, "none")          # column max of |W|: as act_absmax at alpha 0.5 it gives s = 1
+    out = []
+
+    def run(scheme, alpha, act, fold_fn, a_in):
+        fo = fold_fn(a_in, w, 0.5 if alpha is None else alpha, EPS, norm, g, b)
+        gf, bf = fo["gamma_f"], fo["beta_f"]
+        if act == "per-token":
+            xq, xs = sq.sq_norm_quant(x, norm, gf, bf, EPS)
+        elif act == "per-tensor":
+            xq, xs = sq.sq_norm_quant_per_tensor(x, norm, gf, bf, EPS)
+        else:
+            xq, xs = sq.sq_norm_quant_static(x, sq.sq_static_step(a_in, fo["s"]), norm, gf, bf, EPS)
+        y = sq.sq_w8a8_gemm(xq, xs, fo["wq"], fo["w_scale"], out_dtype=torch.float32)
+        err = torch.linalg.norm(y.double() - y_ref).item() / ref_norm
+        out.append({"workload": wl.name, "site": site.name, "scheme": scheme, "alpha": alpha,
+                    "rel_err": float(f"{err:.4g}"), "ordinary_span": ordinary_span(xq, inp["outliers"])})
+
+    run("plain INT8, per-tensor X and W", None, "per-tensor", sq.smoothquant_fold_per_tensor, wmax)
+    run("plain INT8, per-token X, per-channel W", None, "per-token", sq.smoothquant_fold, wmax)
+    for alpha in ALPHAS:
+        run("SmoothQuant O3: static X, per-tensor W", alpha, "static", sq.smoothquant_fold_per_tensor, amax)
+        run("SmoothQuant O2: per-tensor X and W", alpha, "per-tensor", sq.smoothquant_fold_per_tensor, amax)
+        run("SmoothQuant, per-token X, per-channel W", alpha, "per-token", sq.smoothquant_fold, amax)
+    return out
+
+
+def accuracy_study(args):
+    """Plain INT8 against SmoothQuant over alpha on the synthetic stand-ins of every workload."""
+    import torch
+    import w8a8_int8_linear_amd as sq
+    from synth import WORKLOADS
+    for wl_id in sorted(WORKLOADS):
+        wl = WORKLOADS[wl_id]
+        m = min(max(wl.m), args.accuracy_tokens)
+        for si in range(len(wl.sites)):
+            for rec in accuracy_site(torch, sq, wl, si, m):
+                print(json.dumps(rec), flush=True)
+            torch.cuda.empty_cache()
+
+
 class Timer:
     """HIP events on the stream the library launches on, one pair per launch."""
 
@@ -463,6 +543,9 @@ def main():
         return
     if args.granularities:
         granularity_sweep(args)
+        return
+    if args.accuracy:
+        accuracy_study(args)
         return
     import torch
     import w8a8_int8_linear_amd as sq
