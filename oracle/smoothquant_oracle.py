@@ -49,6 +49,15 @@ R14 per-tensor granularity ("SmoothQuant, in depth", "Granularity: O1, O2, O3":
     clip, as the page's failure-mode note on static scales says). The per-row
     and per-channel scale vectors the GEMM reads hold the step repeated, so
     R6 is unchanged.
+R16 the FP8 variant ("LLM.int8() and SmoothQuant", "In papers" / "INT8,
+    Everywhere" on the move to FP8): codes are OCP E4M3 (bias 7, 3 mantissa
+    bits, largest finite 448, no infinities, S.1111.111 is NaN); a per-row step
+    is fl32(absmax / 448) and a code is the round-half-even E4M3 value of
+    fl32(v / step). Magnitudes above 448 round to NaN past the 464 midpoint
+    (448 at the midpoint, ties to even); quotients here never exceed
+    448 * (1 + 2^-23). The GEMM multiplies decoded codes: every product is
+    exact, and the oracle's binary64 sum is exact for K <= 2^17; a binary32
+    accumulator in another order differs by a bounded amount (gemm_fp8_bound).
 R15 the static activation step is fl32(max_j fl32(a_j / s_j) / 127): the
     smoothed input of channel j is y_j / s_j, so its calibration maximum is
     a_j / s_j (a_j from R5, s_j from R4).
@@ -74,6 +83,8 @@ __all__ = [
     "calibrate", "weight_colmax", "smoothing_factors", "fold",
     "int_gemm", "int_gemm_loops", "dequantize", "w8a8_linear",
     "quantize_tensor", "norm_quant_per_tensor", "static_step", "fold_per_tensor",
+    "E4M3_MAX", "e4m3_encode", "e4m3_decode", "quantize_rows_fp8", "norm_quant_fp8", "fold_fp8", "gemm_fp8",
+    "gemm_fp8_bound",
 ]
 
 F32 = np.float32
@@ -412,6 +423,101 @@ def fold_per_tensor(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=
     f["wq"] = wq
     f["w_scale"] = np.full(f["w_hat"].shape[0], st, F32)
     return f
+
+
+# --------------------------------------------------------------------------- FP8 (OCP E4M3) variant (R16)
+
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """binary32 values -> OCP E4M3 codes (uint8), round half to even (reading R16).
+
+    Normal range |v| >= 2^-6: v = m * 2^e with m in [1, 2); the code keeps
+    round_half_even((m - 1) * 8) as its 3-bit mantissa (a carry to 8 moves to
+    the next exponent) under the biased exponent e + 7. Below 2^-6 the spacing
+    is the subnormal 2^-9. Every step is exact in binary64, and numpy's rint
+    rounds half to even. Codes past 0x7E (448) are NaN (0x7F, with the sign).
+    """
+    v = np.asarray(v, dtype=F32)
+    a = np.abs(v).astype(np.float64)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    sub = a < 2.0 ** -6
+    q_sub = np.rint(a * 2.0 ** 9).astype(np.int64)                  # 0 .. 8 (8 is the smallest normal, 0x08)
+    frac, exp = np.frexp(np.where(sub, 1.0, a))                      # a = frac * 2^exp, frac in [0.5, 1)
+    e = exp.astype(np.int64) - 1
+    mant = np.rint((frac * 2.0 - 1.0) * 8.0).astype(np.int64)
+    e = np.where(mant == 8, e + 1, e)
+    mant = np.where(mant == 8, 0, mant)
+    q_norm = (e + 7) * 8 + mant
+    q = np.where(sub, q_sub, q_norm)
+    q = np.where((q > 0x7E) | np.isnan(a), 0x7F, q)
+    return (q | sign).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP E4M3 codes -> binary32 values (exact); 0x7F / 0xFF decode to NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = c & 0x7F
+    ex, mant = mag >> 3, mag & 7
+    val = np.where(ex == 0, mant * 2.0 ** -9, (1.0 + mant / 8.0) * np.exp2(ex - 7.0))
+    val = np.where(mag == 0x7F, np.nan, val)
+    return np.where(c & 0x80, -val, val).astype(F32)
+
+
+def quantize_rows_fp8(y: np.ndarray):
+    """One FP8 step per row: step = fl32(absmax / 448), codes E4M3(fl32(y / step)); a zero step gives 0."""
+    y = np.atleast_2d(np.asarray(y, dtype=F32))
+    amax = np.max(np.abs(y), axis=1) if y.shape[1] else np.zeros(y.shape[0], F32)
+    step = (amax / F32(E4M3_MAX)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (y / step[:, None]).astype(F32)
+    t[step == 0] = 0
+    return e4m3_encode(t), step
+
+
+def norm_quant_fp8(x, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5):
+    """norm_quant with FP8 (E4M3) codes and steps fl32(absmax / 448)."""
+    x32 = widen(x, dtype)
+    if norm == NONE:
+        y = normalize(x32, NONE, gamma=gamma_f)
+        info = {"near_tie": np.zeros(x32.shape[0], bool), "alt": {}}
+    else:
+        mu, var, tie, alt = _stats_block(x32, norm)
+        y = normalize(x32, norm, mu, var, gamma_f, beta_f, eps)
+        info = {"mu": mu, "var": var, "near_tie": tie, "alt": alt}
+    q, step = quantize_rows_fp8(y)
+    info["y"] = y
+    return q, step, info
+
+
+def fold_fp8(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=None, beta=None, s=None):
+    """fold() with FP8 (E4M3) weight codes, one step fl32(max|W-hat row| / 448) per output row."""
+    f = fold(act_absmax, w, dtype, alpha, eps, norm, gamma, beta, s)
+    f["wq"], f["w_scale"] = quantize_rows_fp8(f["w_hat"])
+    return f
+
+
+def gemm_fp8(xq, wq, block: int = 512) -> np.ndarray:
+    """acc[m, n] = sum_k dec(xq[m, k]) * dec(wq[n, k]) exactly (binary64: products of two E4M3
+    values are exact, and their sums are multiples of 2^-18 below 2^35 for K <= 2^17)."""
+    a = e4m3_decode(xq).astype(np.float64)
+    b = e4m3_decode(wq).astype(np.float64)
+    out = np.empty((a.shape[0], b.shape[0]), np.float64)
+    for i in range(0, a.shape[0], block):
+        out[i:i + block] = a[i:i + block] @ b.T
+    return out
+
+
+def gemm_fp8_bound(xq, wq, k_step: int = 128) -> np.ndarray:
+    """Bound on |acc_gpu - acc| for a binary32 accumulation in any order: each of the K/k_step
+    accumulation steps plus a log2(k_step)-deep tree inside one step rounds once, so the error is
+    at most n * 2^-24 * sum_k |x_k w_k| (first order, n = K/k_step + log2(k_step) + 2)."""
+    a = np.abs(e4m3_decode(xq).astype(np.float64))
+    b = np.abs(e4m3_decode(wq).astype(np.float64))
+    k = a.shape[1]
+    n = -(-k // k_step) + int(math.log2(k_step)) + 2
+    return n * 2.0 ** -24 * (a @ b.T)
 
 
 # --------------------------------------------------------------------------- O4 GEMM and epilogue
