@@ -210,6 +210,50 @@ sq_status smoothquant_fold_per_tensor(const float* act_absmax, const void* w, sq
                                       float* s_out, float* gamma_out, float* beta_out,
                                       int8_t* wq, float* w_scale, void* stream);
 
+/*
+ * FP8 variant: the same smoothing with OCP E4M3 codes ("LLM.int8() and
+ * SmoothQuant", section "In papers", and the explainer's chapter on INT8's
+ * legacy: FP8 later took over the role of these INT8 schemes; gfx950 runs it
+ * on its FP8 matrix cores). Codes are E4M3 bytes (bias 7, 3 mantissa bits,
+ * largest finite 448, no infinities), round-half-to-even; a step is
+ * fl32(absmax / 448) per row.
+ */
+
+/*
+ * sq_norm_quant with FP8 codes: arguments as there, and
+ *   xq       [M, K] uint8 out: E4M3 codes of fl32(y / step).
+ *   x_scale  [M] fp32 out: fl32(max_j |y[m, j]| / 448).
+ */
+sq_status sq_norm_quant_fp8(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                            sq_norm norm, const float* gamma_f, const float* beta_f, float eps,
+                            uint8_t* xq, float* x_scale, void* stream);
+
+/*
+ * smoothquant_fold with FP8 weight codes: arguments and s_out, gamma_out,
+ * beta_out as there, and
+ *   wq       [N, K] uint8: E4M3 codes of W-hat = fl32(W * s), one step per row;
+ *   w_scale  [N] fp32: fl32(max_j |W-hat[n, j]| / 448).
+ */
+sq_status smoothquant_fold_fp8(const float* act_absmax, const void* w, sq_dtype w_dt,
+                               int64_t N, int64_t K, double alpha, float eps,
+                               sq_norm norm, const float* gamma, const float* beta,
+                               float* s_out, float* gamma_out, float* beta_out,
+                               uint8_t* wq, float* w_scale, void* stream);
+
+/*
+ * FP8 x FP8 GEMM with the dequantising epilogue:
+ *   y[m, n] = cvt(fl32(fl32(acc * x_scale[m]) * w_scale[n]) (+ bias[n])),
+ *   acc[m, n] = sum_k E4M3(xq[m, k]) * E4M3(wq[n, k]), every product exact and
+ *   the sum accumulated in binary32 in the matrix cores' order (so within a
+ *   bounded distance of the exact sum, not bit-reproducible against another
+ *   order).
+ *   y_dt in {F32, F16, BF16} (no raw I32 mode); K % 128 == 0 in addition to
+ *   the shared limits (SQ_ERR_BAD_SHAPE otherwise).
+ */
+sq_status sq_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
+                      const float* bias, void* y, sq_dtype y_dt,
+                      int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* sq_status_string(sq_status s);
 

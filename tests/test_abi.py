@@ -23,7 +23,8 @@ def _declared():
 def test_header_declares_the_calls():
     assert _declared() == {"smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
                            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step",
-                           "smoothquant_fold_per_tensor", "sq_status_string"}
+                           "smoothquant_fold_per_tensor", "sq_norm_quant_fp8", "smoothquant_fold_fp8",
+                           "sq_fp8_gemm", "sq_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -75,7 +76,24 @@ def foldt(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=No
                                          ws, None)
 
 
+def g8(xq=A, xs=A, wq=A, ws=A, bias=None, y=A, ydt=1, m=16, n=16, k=128):
+    return L.sq_fp8_gemm(xq, xs, wq, ws, bias, y, ydt, m, n, k, None)
+
+
+def nq8(x=A, dt=1, m=16, k=512, norm=0, g=None, b=None, eps=1e-5, xq=A, xs=A):
+    return L.sq_norm_quant_fp8(x, dt, m, k, norm, g, b, F(eps), xq, xs, None)
+
+
+def fold8(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=None, s=A, go=A, bo=None,
+          wq=A, ws=A):
+    return L.smoothquant_fold_fp8(a, w, dt, n, k, ctypes.c_double(alpha), F(eps), norm, g, b, s, go, bo, wq, ws, None)
+
+
 @pytest.mark.parametrize("call,code", [
+    (lambda: g8(ydt=3), 2), (lambda: g8(ydt=9), 2), (lambda: g8(k=192), 3), (lambda: g8(k=64), 3),
+    (lambda: g8(xq=None), 1), (lambda: g8(xs=None), 1), (lambda: g8(m=0), 3), (lambda: g8(y=A4), 4),
+    (lambda: nq8(x=None), 1), (lambda: nq8(dt=3), 2), (lambda: nq8(k=100), 3), (lambda: nq8(norm=0, b=A), 5),
+    (lambda: fold8(wq=None), 1), (lambda: fold8(alpha=2.0), 5), (lambda: fold8(dt=3), 2),
     (lambda: nqt(x=None), 1), (lambda: nqt(xs=None), 1), (lambda: nqt(dt=3), 2), (lambda: nqt(k=100), 3),
     (lambda: nqt(xq=A4), 4), (lambda: nqt(norm=0, b=A), 5), (lambda: nqt(norm=1, eps=0.0), 5),
     (lambda: nqs(step=None), 1), (lambda: nqs(x=None), 1), (lambda: nqs(dt=7), 2), (lambda: nqs(m=0), 3),

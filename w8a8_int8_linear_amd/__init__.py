@@ -18,8 +18,11 @@ from ._lib import (  # noqa: F401
     lib,
     smoothquant_calibrate,
     smoothquant_fold,
+    smoothquant_fold_fp8,
     smoothquant_fold_per_tensor,
+    sq_fp8_gemm,
     sq_norm_quant,
+    sq_norm_quant_fp8,
     sq_norm_quant_per_tensor,
     sq_norm_quant_static,
     sq_static_step,

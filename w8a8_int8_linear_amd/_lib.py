@@ -26,7 +26,7 @@ _NORM = {"none": SQ_NORM_NONE, "layernorm": SQ_NORM_LAYERNORM, "rmsnorm": SQ_NOR
 
 EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step", "smoothquant_fold_per_tensor",
-           "sq_status_string")
+           "sq_norm_quant_fp8", "smoothquant_fold_fp8", "sq_fp8_gemm", "sq_status_string")
 
 
 class SmoothQuantError(RuntimeError):
@@ -37,7 +37,8 @@ class SmoothQuantError(RuntimeError):
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m w8a8_int8_linear_amd.build`")
+        raise ImportError(f"{path} is missing: build it with `python w8a8_int8_linear_amd/build.py` "
+                          "(or __graft_entry__.build())")
     lib = ctypes.CDLL(path)
     P, I64, F, D, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_int
     lib.smoothquant_calibrate.argtypes = [P, I, I64, I64, I, P, P, F, P, P]
@@ -48,6 +49,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sq_norm_quant_static.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P]
     lib.sq_static_step.argtypes = [P, P, I64, P, P]
     lib.smoothquant_fold_per_tensor.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
+    lib.sq_norm_quant_fp8.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P]
+    lib.smoothquant_fold_fp8.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
+    lib.sq_fp8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
     lib.sq_status_string.argtypes = [I]
     lib.sq_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -115,6 +119,11 @@ def smoothquant_fold(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, be
     return _fold("smoothquant_fold", act_absmax, w, alpha, eps, norm, gamma, beta, out)
 
 
+def smoothquant_fold_fp8(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, beta=None, out=None):
+    """As smoothquant_fold with FP8 (OCP E4M3) weight codes (wq uint8) and steps absmax / 448."""
+    return _fold("smoothquant_fold_fp8", act_absmax, w, alpha, eps, norm, gamma, beta, out)
+
+
 def smoothquant_fold_per_tensor(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, beta=None, out=None):
     """As smoothquant_fold with one weight step for the whole tensor (w_scale holds it repeated)."""
     return _fold("smoothquant_fold_per_tensor", act_absmax, w, alpha, eps, norm, gamma, beta, out)
@@ -134,10 +143,11 @@ def _fold(fn, act_absmax, w, alpha, eps, norm, gamma, beta, out):
         out.setdefault("beta_f", torch.empty(k, dtype=torch.float32, device=dev))
     else:
         out["beta_f"] = None
-    out.setdefault("wq", torch.empty(n, k, dtype=torch.int8, device=dev))
+    code_dt = torch.uint8 if fn.endswith("_fp8") else torch.int8
+    out.setdefault("wq", torch.empty(n, k, dtype=code_dt, device=dev))
     out.setdefault("w_scale", torch.empty(n, dtype=torch.float32, device=dev))
     for key, shp, dt in [("s", (k,), torch.float32), ("gamma_f", (k,), torch.float32),
-                         ("beta_f", (k,), torch.float32), ("wq", (n, k), torch.int8), ("w_scale", (n,), torch.float32)]:
+                         ("beta_f", (k,), torch.float32), ("wq", (n, k), code_dt), ("w_scale", (n,), torch.float32)]:
         _dev(out[key], key, dt, shp)
     with torch.cuda.device(dev):
         _check(fn, getattr(lib, fn)(
@@ -150,6 +160,11 @@ def _fold(fn, act_absmax, w, alpha, eps, norm, gamma, beta, out):
 def sq_norm_quant(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
     """Fused norm (folded gamma', beta') + per-token INT8: returns (xq [M, K] int8, x_scale [M] fp32)."""
     return _nq("sq_norm_quant", x, norm, gamma_f, beta_f, eps, xq, x_scale)
+
+
+def sq_norm_quant_fp8(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
+    """Fused norm + per-token FP8 (OCP E4M3): returns (xq [M, K] uint8 codes, x_scale [M] fp32 = absmax / 448)."""
+    return _nq("sq_norm_quant_fp8", x, norm, gamma_f, beta_f, eps, xq, x_scale)
 
 
 def sq_norm_quant_per_tensor(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
@@ -181,11 +196,12 @@ def _nq(fn, x, norm, gamma_f, beta_f, eps, xq, x_scale, *step):
     m, k = x.shape
     _dev(gamma_f, "gamma_f", torch.float32, (k,))
     _dev(beta_f, "beta_f", torch.float32, (k,))
+    code_dt = torch.uint8 if fn.endswith("_fp8") else torch.int8
     if xq is None:
-        xq = torch.empty(m, k, dtype=torch.int8, device=x.device)
+        xq = torch.empty(m, k, dtype=code_dt, device=x.device)
     if x_scale is None:
         x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
-    _dev(xq, "xq", torch.int8, (m, k))
+    _dev(xq, "xq", code_dt, (m, k))
     _dev(x_scale, "x_scale", torch.float32, (m,))
     with torch.cuda.device(x.device):
         _check(fn, getattr(lib, fn)(
@@ -211,6 +227,27 @@ def sq_w8a8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.float16, y
     _dev(y, "y", out_dtype, (m, n))
     with torch.cuda.device(xq.device):
         _check("sq_w8a8_gemm", lib.sq_w8a8_gemm(
+            _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DT[y.dtype], m, n, k,
+            _stream(xq)))
+    return y
+
+
+def sq_fp8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.float16, y=None):
+    """y [M, N] = dequant(E4M3(xq) @ E4M3(wq)^T), binary32 accumulation; xq, wq uint8 E4M3 codes."""
+    _dev(xq, "xq", torch.uint8)
+    _dev(wq, "wq", torch.uint8)
+    m, k = xq.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
+    _dev(x_scale, "x_scale", torch.float32, (m,))
+    _dev(w_scale, "w_scale", torch.float32, (n,))
+    _dev(bias, "bias", torch.float32, (n,))
+    if y is None:
+        y = torch.empty(m, n, dtype=out_dtype, device=xq.device)
+    _dev(y, "y", out_dtype, (m, n))
+    with torch.cuda.device(xq.device):
+        _check("sq_fp8_gemm", lib.sq_fp8_gemm(
             _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DT[y.dtype], m, n, k,
             _stream(xq)))
     return y

@@ -36,8 +36,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // ----------------------------------------------------------------------------- epilogue
 
 // Four consecutive outputs y[m, n .. n+3] of one lane (n % 4 == 0).
-template <int YDT>
-__device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n, const v4i acc, float xs,
+template <int YDT, typename AccV = v4i>
+__device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n, const AccV acc, float xs,
                                        const float* __restrict__ ws, const float* __restrict__ bias) {
   const int64_t off = static_cast<int64_t>(m) * N + n;
   const bool full = (n + 3 < N) && ((N & 3) == 0);
@@ -454,6 +454,109 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   }
 }
 
+// ----------------------------------------------------------------------------- FP8 (OCP E4M3) tiled kernel
+
+// FP8 operands through the same tile, DMA ring, swizzle and XCD mapping as
+// k_gemm_tile, multiplied by v_mfma_scale_f32_16x16x128_f8f6f4 (format 0 =
+// E4M3 for both operands, block scales 2^0) into binary32 accumulators. One
+// MFMA takes a whole 128-byte stage: lane group g supplies the stage's K bytes
+// 16g .. 16g+15 and 64+16g .. 64+16g+15 of its row for both operands (the
+// chunks the INT8 kernel reads for its two K steps), so every product pairs
+// the same K index. The stage loop waits for stage s, passes one barrier (after
+// which every wave is done with stage s-1's buffer), refills that buffer with
+// stage s+1, then reads stage s's fragments and multiplies. Requires K % 128 == 0.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <int YDT>
+__global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                          const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+                                                          const float* __restrict__ bias, void* __restrict__ y, int M,
+                                                          int N, int K, int tiles_m, int tiles_n, int group) {
+  __shared__ __attribute__((aligned(1024))) int8_t lA0[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lA1[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB0[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB1[kStage2Bytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int tm, tn;
+  map_tile(blockIdx.x, tiles_m * tiles_n, tiles_m, group, tm, tn);
+  const int m0 = tm * kTile, n0 = tn * kTile;
+  uint32_t a_off[kDma2PerWave], b_off[kDma2PerWave];
+#pragma unroll
+  for (int i = 0; i < kDma2PerWave; ++i) {
+    const int r = (wid * kDma2PerWave + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz2(r);
+    a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
+    b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
+  }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
+  const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
+  const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
+  int a_rd[2], b_rd[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int c = 4 * t + (lane >> 4);
+    a_rd[t] = rra * kSlice2 + 16 * (c ^ swz2(rra));
+    b_rd[t] = rrb * kSlice2 + 16 * (c ^ swz2(rrb));
+  }
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int ns = K / kSlice2;
+  const int last = (ns - 1) * kSlice2;
+  issue_stage2(ra, lA0, a_off, 0, wid);
+  issue_stage2(rb, lB0, b_off, 0, wid);
+#define SQ_FP8_STAGE(LA, LB, LA_NXT, LB_NXT)                                                              \
+  {                                                                                                      \
+    __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0): stage s landed, stage s-1 reads done */ \
+    stage_barrier();                                                                                     \
+    const int kn = min((s + 1) * kSlice2, last);                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                                   \
+    issue_stage2(ra, LA_NXT, a_off, kn, wid);                                                            \
+    issue_stage2(rb, LB_NXT, b_off, kn, wid);                                                            \
+    v4i fb[2][TJ];                                                                                       \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                        \
+      _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                                     \
+        fb[t][j] = *reinterpret_cast<const v4i*>(LB + b_rd[t] + j * 16 * kSlice2);                       \
+    _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                                     \
+      const v4i a0 = *reinterpret_cast<const v4i*>(LA + a_rd[0] + i * 16 * kSlice2);                    \
+      const v4i a1 = *reinterpret_cast<const v4i*>(LA + a_rd[1] + i * 16 * kSlice2);                    \
+      const v8i av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);                            \
+      _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                                   \
+        const v8i bv = __builtin_shufflevector(fb[0][j], fb[1][j], 0, 1, 2, 3, 4, 5, 6, 7);              \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 127, 0, 127); \
+      }                                                                                                  \
+    }                                                                                                    \
+    ++s;                                                                                                 \
+  }
+  int s = 0;
+  for (; s + 2 <= ns;) {
+    SQ_FP8_STAGE(lA0, lB0, lA1, lB1)
+    SQ_FP8_STAGE(lA1, lB1, lA0, lB0)
+  }
+  if (s < ns) SQ_FP8_STAGE(lA0, lB0, lA1, lB1)
+#undef SQ_FP8_STAGE
+  __builtin_amdgcn_s_waitcnt(0x0070);     // no DMA into LDS outlives the loop
+
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int m = m0 + wm + 16 * i + (lane & 15);
+    if (m >= M) continue;
+    const float xsm = xs[m];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+      if (n < N) store4<YDT>(y, N, m, n, acc[i][j], xsm, ws, bias);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- decode helpers
 
 // Decode shapes (M <= 64) are bound by streaming wq once from HBM. HBM and the
@@ -815,6 +918,27 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
 }
 
 }  // namespace
+
+template <int YDT>
+hipError_t launch_fp8_typed(const GemmArgs& g, hipStream_t st) {
+  const int tiles_m = (g.M + kTile - 1) / kTile;
+  const int tiles_n = (g.N + kTile - 1) / kTile;
+  const int group = min(tiles_m, 8);
+  hipLaunchKernelGGL((k_gemm_tile_fp8<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st,
+                     reinterpret_cast<const uint8_t*>(g.xq), g.x_scale, reinterpret_cast<const uint8_t*>(g.wq),
+                     g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
+  if (g.K % kSlice2 != 0) return hipErrorInvalidValue;
+  switch (g.y_dt) {
+    case SQ_DT_F32: return launch_fp8_typed<SQ_DT_F32>(g, st);
+    case SQ_DT_F16: return launch_fp8_typed<SQ_DT_F16>(g, st);
+    case SQ_DT_BF16: return launch_fp8_typed<SQ_DT_BF16>(g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   switch (g.y_dt) {

@@ -11,6 +11,8 @@
 // workgroup fits on a CU (a 20480-wide binary32 row is 80 KiB of registers).
 #pragma once
 
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq_launch.h"
 #include "smoothquant.h"
@@ -233,7 +235,7 @@ __device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
 //        and refill vector i right after its codes are written.
 //  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
 //        normalise in place, then max and codes.
-template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
+template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS, bool FP8 = false>
 __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
                                              int64_t row, int64_t next, int M, int K,
                                              const float* __restrict__ gamma,
@@ -282,9 +284,9 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
     for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
     amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
-    const float step = int8_step(amax);
+    const float step = FP8 ? fp8_step(amax) : int8_step(amax);
     if (threadIdx.x == 0) x_scale[row] = step;
-    const Quantizer qz(step);
+    const typename std::conditional<FP8, QuantizerFp8, Quantizer>::type qz(step);
     if constexpr (kKeepY) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
@@ -330,9 +332,9 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
     for (int i = 0; i < NV; ++i) amax = fmaxf(amax, pm[i]);
     amax = block_max<THREADS>(amax, reinterpret_cast<float*>(red.at(rk++)));
-    const float step = int8_step(amax);
+    const float step = FP8 ? fp8_step(amax) : int8_step(amax);
     if (threadIdx.x == 0) x_scale[row] = step;
-    const Quantizer qz(step);
+    const typename std::conditional<FP8, QuantizerFp8, Quantizer>::type qz(step);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * THREADS;
@@ -345,6 +347,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 constexpr int kRowsPerRow = 0;       // one step per row (per-token activations, per-channel weights)
 constexpr int kRowsAmax = 1;         // per-tensor first pass: each row's max |y| into x_scale[row]; no codes
 constexpr int kRowsGivenStep = 2;    // per-tensor codes with a step given for the whole tensor, clipped
+constexpr int kRowsFp8 = 3;          // one step per row, FP8 (OCP E4M3) codes: step = absmax / 448
 
 // One row of a per-tensor pass: MODE kRowsAmax writes the row's max |y| alone
 // (the first pass of a per-tensor dynamic step); kRowsGivenStep writes the
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
   raw.load(x, blockIdx.x, K);
   gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
   int rk = 0;
-  if constexpr (MODE != kRowsPerRow) {
+  if constexpr (MODE == kRowsAmax || MODE == kRowsGivenStep) {
     // per-tensor passes (step_ptr and write_scale are used only here)
     const Quantizer qz(MODE == kRowsGivenStep ? *step_ptr : 0.0f);
     for (int64_t row = blockIdx.x; row < M; row += G)
@@ -481,7 +484,8 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
                                                       red, rk, qz, write_scale != 0);
   } else {
     for (int64_t row = blockIdx.x; row < M; row += G)
-      quantize_row<T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk);
+      quantize_row<T, NORM, NV, THREADS, kReg, kLds, MODE == kRowsFp8>(raw, x, row, row + G, M, K, gamma, gv, beta,
+                                                                       eps, xq, x_scale, red, rk);
   }
 }
 

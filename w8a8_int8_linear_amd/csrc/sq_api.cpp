@@ -94,6 +94,41 @@ sq_status smoothquant_fold_per_tensor(const float* act_absmax, const void* w, sq
   return from_hip(sq::launch_norm_quant_per_tensor(q, st));
 }
 
+sq_status sq_norm_quant_fp8(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm, const float* gamma_f,
+                            const float* beta_f, float eps, uint8_t* xq, float* x_scale, void* stream) {
+  int8_t* q = reinterpret_cast<int8_t*>(xq);
+  if (sq_status s = sq::check_norm_quant(x, x_dt, M, K, norm, gamma_f, beta_f, eps, q, x_scale)) return s;
+  sq::RowArgs a{x, x_dt, M, static_cast<int>(K), norm, gamma_f, beta_f, eps, q, x_scale, nullptr};
+  return from_hip(sq::launch_norm_quant_fp8(a, as_stream(stream)));
+}
+
+sq_status smoothquant_fold_fp8(const float* act_absmax, const void* w, sq_dtype w_dt, int64_t N, int64_t K,
+                               double alpha, float eps, sq_norm norm, const float* gamma, const float* beta,
+                               float* s_out, float* gamma_out, float* beta_out, uint8_t* wq, float* w_scale,
+                               void* stream) {
+  int8_t* q = reinterpret_cast<int8_t*>(wq);
+  if (sq_status s = sq::check_fold(act_absmax, w, w_dt, N, K, alpha, eps, norm, gamma, beta, s_out, gamma_out,
+                                   beta_out, q, w_scale))
+    return s;
+  hipStream_t st = as_stream(stream);
+  sq::FoldArgs f{act_absmax, w, w_dt, N, K, alpha, eps, gamma, beta, s_out, gamma_out, beta_out};
+  if (sq_status s = from_hip(sq::launch_fold_colmax_scales(f, st))) return s;
+  sq::RowArgs r{w, w_dt, N, static_cast<int>(K), SQ_NORM_NONE, s_out, nullptr, 1.0f, q, w_scale, nullptr};
+  return from_hip(sq::launch_norm_quant_fp8(r, st));
+}
+
+sq_status sq_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
+                      const float* bias, void* y, sq_dtype y_dt, int64_t M, int64_t N, int64_t K, void* stream) {
+  const int8_t* xa = reinterpret_cast<const int8_t*>(xq);
+  const int8_t* wa = reinterpret_cast<const int8_t*>(wq);
+  if (y_dt == SQ_DT_I32) return SQ_ERR_BAD_DTYPE;
+  if (sq_status s = sq::check_gemm(xa, x_scale, wa, w_scale, bias, y, y_dt, M, N, K)) return s;
+  if (K % 128 != 0) return SQ_ERR_BAD_SHAPE;
+  sq::GemmArgs g{xa, x_scale, wa, w_scale, bias, y, y_dt, static_cast<int>(M), static_cast<int>(N),
+                 static_cast<int>(K)};
+  return from_hip(sq::launch_gemm_fp8(g, as_stream(stream)));
+}
+
 const char* sq_status_string(sq_status s) {
   switch (s) {
     case SQ_OK: return "SQ_OK";

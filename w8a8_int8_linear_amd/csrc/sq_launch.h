@@ -54,6 +54,10 @@ hipError_t launch_calibrate(const RowArgs& a, hipStream_t st);
 // norm_quant pass over W with gamma = s).
 hipError_t launch_fold_colmax_scales(const FoldArgs& f, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// FP8 (OCP E4M3) variants: per-row steps absmax / 448 and E4M3 codes (xq, wq hold
+// the code bytes); the GEMM accumulates in binary32 and needs K % 128 == 0.
+hipError_t launch_norm_quant_fp8(const RowArgs& a, hipStream_t st);
+hipError_t launch_gemm_fp8(const GemmArgs& g, hipStream_t st);
 // One step for the whole tensor: the rows' maxima, their max, then the codes;
 // x_scale ends holding the step in every entry.
 hipError_t launch_norm_quant_per_tensor(const RowArgs& a, hipStream_t st);
