@@ -55,6 +55,10 @@ def parse():
     p.add_argument("--accuracy-tokens", type=int, default=256, help="token rows per site in the accuracy study")
     p.add_argument("--summarize-granularities", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --granularities into a profiles/ table and exit")
+    p.add_argument("--fp8", action="store_true",
+                   help="INT8 against FP8 (E4M3) per stage on the MT-NLG-530B-width sites (HIP-event medians) and exit")
+    p.add_argument("--summarize-fp8", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace --stats of --fp8 into a profiles/ table and exit")
     return p.parse_args()
 
 
@@ -250,6 +254,23 @@ GRAN_CMD = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format cs
             "python3 bench.py --granularities")
 
 
+def median_ms(torch, fn, n):
+    """Median of n launches of fn, each between a pair of HIP events, after one untimed launch."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def granularity_sweep(args):
     """Per-token vs per-tensor dynamic vs static activation steps (and per-channel vs per-tensor weight
     steps in the fold) on the MT-NLG-width sites, HIP-event medians over 20 launches (fold: 5)."""
@@ -260,19 +281,7 @@ def granularity_sweep(args):
     sites = build_sites(torch, sq, wl, wl.m[0])
 
     def med(fn, n):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(n):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        ts.sort()
-        return ts[len(ts) // 2]
+        return median_ms(torch, fn, n)
 
     for d in sites:
         m, k, n, norm = d["m"], d["k"], d["n"], d["norm"]
@@ -301,29 +310,101 @@ def granularity_sweep(args):
                               "ms": round(ms, 4), "GBps": round(fold_bytes / ms / 1e6, 1)}), flush=True)
 
 
-def summarize_granularities(trace_dir):
-    """Kernel statistics of a --granularities run as a profiles/ table."""
+def kernel_stats_table(trace_dir, title, cmd, flag, note, out_name):
+    """A rocprofv3 --kernel-trace --stats run's per-kernel statistics as a profiles/ table."""
     import csv
     import glob
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no kernel stats under {trace_dir}")
-    lines = ["# rocprofv3 kernel statistics: activation and weight step granularities, MT-NLG-530B-width sites", "",
-             f"Command: `{GRAN_CMD}`, then `python bench.py --summarize-granularities <dir>`.", "",
-             "Sites: LayerNorm 8192x20480 -> fc1 and NONE 8192x81920 -> fc2 (fp16), folds of their weights "
-             "(81920x20480, 20480x81920). The last template argument of `k_norm_quant` is its mode: 0 one step per "
-             "row, 1 the rows' maxima (first per-tensor pass), 2 codes with a step given for the whole tensor "
-             "(second per-tensor pass, or a static step); `k_tensor_step` reduces the rows' maxima to the tensor "
-             "step.", "",
+    lines = [f"# rocprofv3 kernel statistics: {title}", "",
+             f"Command: `{cmd}`, then `python bench.py {flag} <dir>`.", "", note, "",
              "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(hits[0])):
         if "sq::" in r["Name"]:
             short = r["Name"].split("(")[0].replace("void ", "")
             lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                          f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} |")
-    with open(os.path.join(ROOT, "profiles", "kernel_stats_granularities_mtnlg530b.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_granularities(trace_dir):
+    """Kernel statistics of a --granularities run as a profiles/ table."""
+    kernel_stats_table(
+        trace_dir, "activation and weight step granularities, MT-NLG-530B-width sites", GRAN_CMD,
+        "--summarize-granularities",
+        "Sites: LayerNorm 8192x20480 -> fc1 and NONE 8192x81920 -> fc2 (fp16), folds of their weights "
+        "(81920x20480, 20480x81920). The last template argument of `k_norm_quant` is its mode: 0 one step per "
+        "row, 1 the rows' maxima (first per-tensor pass), 2 codes with a step given for the whole tensor "
+        "(second per-tensor pass, or a static step); `k_tensor_step` reduces the rows' maxima to the tensor "
+        "step.", "kernel_stats_granularities_mtnlg530b.md")
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3) against INT8
+
+FP8_CMD = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+           "python3 bench.py --fp8")
+
+
+def fp8_sweep(args):
+    """INT8 against FP8 (OCP E4M3) for each stage of the MT-NLG-width sites, HIP-event medians over
+    20 launches (fold: 5). Both GEMMs are priced against the same 5.0 POP/s dense peak."""
+    import torch
+    import w8a8_int8_linear_amd as sq
+    from synth import WORKLOADS
+    wl = WORKLOADS[5]
+    sites = build_sites(torch, sq, wl, wl.m[0])
+    for d in sites:
+        m, k, n, norm = d["m"], d["k"], d["n"], d["norm"]
+        amax = sq.smoothquant_calibrate(d["x_cal"], norm, d["gamma"], d["beta"], EPS)
+        f8 = {key: (torch.empty_like(v, dtype=torch.uint8) if key == "wq" else torch.empty_like(v))
+              for key, v in d["fold"].items()}
+        fo = sq.smoothquant_fold(amax, d["w"], wl.alpha, EPS, norm, d["gamma"], d["beta"], out=d["fold"])
+        sq.smoothquant_fold_fp8(amax, d["w"], wl.alpha, EPS, norm, d["gamma"], d["beta"], out=f8)
+        g, b = fo["gamma_f"], fo["beta_f"]
+        xq8 = torch.empty(m, k, dtype=torch.uint8, device="cuda")
+        xs8 = torch.empty(m, dtype=torch.float32, device="cuda")
+        e = d["x"].element_size()
+        o = d["y"].element_size()
+        sizes = {"norm_quant": m * k * e + m * k + 4 * m + 4 * k * (2 if b is not None else 1),
+                 "fold": 2 * n * k * e + n * k + 4 * n + 16 * k,
+                 "gemm": n * k + 4 * n + m * k + 4 * m + o * m * n}
+        stages = [
+            ("norm_quant", "int8", 20, lambda: sq.sq_norm_quant(d["x"], norm, g, b, EPS, d["xq"], d["xs"])),
+            ("norm_quant", "fp8", 20, lambda: sq.sq_norm_quant_fp8(d["x"], norm, g, b, EPS, xq8, xs8)),
+            ("fold", "int8", 5, lambda: sq.smoothquant_fold(amax, d["w"], wl.alpha, EPS, norm, d["gamma"], d["beta"],
+                                                            out=d["fold"])),
+            ("fold", "fp8", 5, lambda: sq.smoothquant_fold_fp8(amax, d["w"], wl.alpha, EPS, norm, d["gamma"],
+                                                               d["beta"], out=f8)),
+            ("gemm", "int8", 20, lambda: sq.sq_w8a8_gemm(d["xq"], d["xs"], fo["wq"], fo["w_scale"], y=d["y"],
+                                                         out_dtype=d["y"].dtype)),
+            ("gemm", "fp8", 20, lambda: sq.sq_fp8_gemm(xq8, xs8, f8["wq"], f8["w_scale"], y=d["y"],
+                                                       out_dtype=d["y"].dtype)),
+        ]
+        for stage, fmt, reps, fn in stages:
+            ms = median_ms(torch, fn, reps)
+            rec = {"stage": stage, "format": fmt, "site": d["site"].name, "ms": round(ms, 4),
+                   "GBps": round(sizes[stage] / ms / 1e6, 1)}
+            if stage == "gemm":
+                tops = 2.0 * m * n * k / ms / 1e9
+                rec.update(shape=[m, n, k], TOPS=round(tops, 1), frac=round(tops / 5000.0, 4))
+            else:
+                rec["shape"] = [m, k] if stage == "norm_quant" else [n, k]
+            print(json.dumps(rec), flush=True)
+        del f8, xq8, xs8
+        torch.cuda.empty_cache()
+
+
+def summarize_fp8(trace_dir):
+    kernel_stats_table(
+        trace_dir, "INT8 against FP8 (OCP E4M3), MT-NLG-530B-width sites", FP8_CMD, "--summarize-fp8",
+        "Sites: LayerNorm 8192x20480 -> fc1 (N 81920) and NONE 8192x81920 -> fc2 (N 20480), fp16. "
+        "`k_norm_quant` mode 0 is the INT8 per-token quantiser and mode 3 the FP8 one; `k_gemm_tile` is the "
+        "INT8 GEMM (v_mfma_i32_16x16x64_i8) and `k_gemm_tile_fp8` the FP8 one "
+        "(v_mfma_scale_f32_16x16x128_f8f6f4); the fold's kernels are shared but for the weight quantiser.",
+        "kernel_stats_fp8_mtnlg530b.md")
 
 
 # ----------------------------------------------------------------------------- accuracy study
@@ -354,6 +435,16 @@ def ordinary_span(xq, outliers):
     return int(xq[:, keep].abs().amax(dim=1).median().item())
 
 
+def ordinary_span_fp8(xq, outliers):
+    """As ordinary_span for FP8 (E4M3) codes: the median over tokens of the largest decoded |code|
+    among the non-outlier channels, out of 448."""
+    import torch
+    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().to(xq.device)
+    keep = torch.ones(xq.shape[1], dtype=torch.bool, device=xq.device)
+    keep[torch.as_tensor(outliers, dtype=torch.long, device=xq.device)] = False
+    return float(table[xq[:, keep].long()].abs().amax(dim=1).median().item())
+
+
 def accuracy_site(torch, sq, wl, si, m_tokens):
     """One site: relative output error and ordinary-channel span for each scheme."""
     from synth import site_inputs
@@ -369,16 +460,22 @@ def accuracy_site(torch, sq, wl, si, m_tokens):
     def run(scheme, alpha, act, fold_fn, a_in):
         fo = fold_fn(a_in, w, 0.5 if alpha is None else alpha, EPS, norm, g, b)
         gf, bf = fo["gamma_f"], fo["beta_f"]
-        if act == "per-token":
-            xq, xs = sq.sq_norm_quant(x, norm, gf, bf, EPS)
-        elif act == "per-tensor":
-            xq, xs = sq.sq_norm_quant_per_tensor(x, norm, gf, bf, EPS)
+        if act == "fp8":
+            xq, xs = sq.sq_norm_quant_fp8(x, norm, gf, bf, EPS)
+            y = sq.sq_fp8_gemm(xq, xs, fo["wq"], fo["w_scale"], out_dtype=torch.float32)
+            span = ordinary_span_fp8(xq, inp["outliers"])
         else:
-            xq, xs = sq.sq_norm_quant_static(x, sq.sq_static_step(a_in, fo["s"]), norm, gf, bf, EPS)
-        y = sq.sq_w8a8_gemm(xq, xs, fo["wq"], fo["w_scale"], out_dtype=torch.float32)
+            if act == "per-token":
+                xq, xs = sq.sq_norm_quant(x, norm, gf, bf, EPS)
+            elif act == "per-tensor":
+                xq, xs = sq.sq_norm_quant_per_tensor(x, norm, gf, bf, EPS)
+            else:
+                xq, xs = sq.sq_norm_quant_static(x, sq.sq_static_step(a_in, fo["s"]), norm, gf, bf, EPS)
+            y = sq.sq_w8a8_gemm(xq, xs, fo["wq"], fo["w_scale"], out_dtype=torch.float32)
+            span = ordinary_span(xq, inp["outliers"])
         err = torch.linalg.norm(y.double() - y_ref).item() / ref_norm
         out.append({"workload": wl.name, "site": site.name, "scheme": scheme, "alpha": alpha,
-                    "rel_err": float(f"{err:.4g}"), "ordinary_span": ordinary_span(xq, inp["outliers"])})
+                    "rel_err": float(f"{err:.4g}"), "ordinary_span": span})
 
     run("plain INT8, per-tensor X and W", None, "per-tensor", sq.smoothquant_fold_per_tensor, wmax)
     run("plain INT8, per-token X, per-channel W", None, "per-token", sq.smoothquant_fold, wmax)
@@ -386,6 +483,10 @@ def accuracy_site(torch, sq, wl, si, m_tokens):
         run("SmoothQuant O3: static X, per-tensor W", alpha, "static", sq.smoothquant_fold_per_tensor, amax)
         run("SmoothQuant O2: per-tensor X and W", alpha, "per-tensor", sq.smoothquant_fold_per_tensor, amax)
         run("SmoothQuant, per-token X, per-channel W", alpha, "per-token", sq.smoothquant_fold, amax)
+    if site.k % 128 == 0:
+        run("plain FP8 (E4M3), per-token X, per-channel W", None, "fp8", sq.smoothquant_fold_fp8, wmax)
+        for alpha in ALPHAS:
+            run("SmoothQuant FP8 (E4M3), per-token X, per-channel W", alpha, "fp8", sq.smoothquant_fold_fp8, amax)
     return out
 
 
@@ -534,6 +635,9 @@ def main():
     if args.summarize_granularities:
         summarize_granularities(args.summarize_granularities)
         return
+    if args.summarize_fp8:
+        summarize_fp8(args.summarize_fp8)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",
                           "n_gpus": args.gpus}))
@@ -543,6 +647,9 @@ def main():
         return
     if args.granularities:
         granularity_sweep(args)
+        return
+    if args.fp8:
+        fp8_sweep(args)
         return
     if args.accuracy:
         accuracy_study(args)

@@ -1,5 +1,5 @@
-"""The synthetic accuracy study (plain INT8 against SmoothQuant over alpha): its binary64
-reference and its level metric on the CPU, and on the GPU the construction it uses for plain
+"""The synthetic accuracy study (plain INT8 and FP8 against SmoothQuant over alpha): its binary64
+reference and its level metrics on the CPU, and on the GPU the construction it uses for plain
 INT8 (s = 1 exactly) and the agreement of its hot-path errors with the oracle's pipeline."""
 import numpy as np
 import pytest
@@ -33,6 +33,13 @@ def test_ordinary_span():
     xq = torch.tensor([[3, -120, 5, 0], [1, 127, -7, 2], [0, 90, 2, -1]], dtype=torch.int8)
     # channel 1 is the outlier; the rest reach 5, 7, 2 -> median 5
     assert bench.ordinary_span(xq, [1]) == 5
+
+
+def test_ordinary_span_fp8():
+    # E4M3 codes: 0x38 = 1, 0x40 = 2, 0x48 = 4, 0x30 = 0.5, 0x01 = 2^-9, 0xB8 = -1, 0x7E = 448
+    xq = torch.tensor([[0x38, 0x7E, 0x40, 0x00], [0xB8, 0x7E, 0x30, 0x01], [0x00, 0xFE, 0x48, 0x00]], dtype=torch.uint8)
+    # channel 1 is the outlier; the rest reach 2, 1, 4 -> median 2
+    assert bench.ordinary_span_fp8(xq, [1]) == 2.0
 
 
 @pytest.mark.gpu

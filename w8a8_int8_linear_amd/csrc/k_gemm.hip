@@ -462,11 +462,34 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
 // MFMA takes a whole 128-byte stage: lane group g supplies the stage's K bytes
 // 16g .. 16g+15 and 64+16g .. 64+16g+15 of its row for both operands (the
 // chunks the INT8 kernel reads for its two K steps), so every product pairs
-// the same K index. The stage loop waits for stage s, passes one barrier (after
-// which every wave is done with stage s-1's buffer), refills that buffer with
-// stage s+1, then reads stage s's fragments and multiplies. Requires K % 128 == 0.
+// the same K index. Requires K % 128 == 0.
+//
+// A stage's fragments (8 A and 4 B blocks of 32 bytes per lane, 96 VGPRs)
+// cannot be double-buffered beside the 128 accumulator VGPRs, so the stage
+// keeps its B blocks and streams A one row block ahead of the MFMAs: while
+// the four MFMAs of block i run, block i+1 is read. After the last block's
+// MFMAs are issued the wave waits for stage s+1 (the only DMA in flight) and
+// for its own reads of stage s, passes the barrier (every wave is then done
+// with stage s's buffer, and stage s+1 is visible), refills that buffer with
+// stage s+2, and reads stage s+1's B blocks and first A block while those
+// MFMAs drain. Issue indices are clamped to the last stage; the final issues
+// and reads are harmless reloads.
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i lds_frag8(const int8_t* base, int off0, int off1) {
+  const v4i lo = *reinterpret_cast<const v4i*>(base + off0);
+  const v4i hi = *reinterpret_cast<const v4i*>(base + off1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Four MFMAs of A block i against the stage's B blocks, while block i+1 is read
+// (the read goes out first, then the MFMAs, in that order).
+__device__ __forceinline__ void fp8_block(v4f (&acc)[TJ], const v8i& a, const v8i (&fb)[TJ]) {
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+    acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], a, acc[j], 0, 0, 0, 127, 0, 127);
+}
 
 template <int YDT>
 __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
@@ -512,27 +535,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
   const int last = (ns - 1) * kSlice2;
   issue_stage2(ra, lA0, a_off, 0, wid);
   issue_stage2(rb, lB0, b_off, 0, wid);
+  memory_opaque();
+  issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
+  issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
+  __builtin_amdgcn_s_waitcnt(0x0F78);     // vmcnt(8): stage 0 landed
+  stage_barrier();
+  v8i fb[TJ], a_cur;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) fb[j] = lds_frag8(lB0 + j * 16 * kSlice2, b_rd[0], b_rd[1]);
+  a_cur = lds_frag8(lA0, a_rd[0], a_rd[1]);
+
 #define SQ_FP8_STAGE(LA, LB, LA_NXT, LB_NXT)                                                              \
   {                                                                                                      \
-    __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0): stage s landed, stage s-1 reads done */ \
-    stage_barrier();                                                                                     \
-    const int kn = min((s + 1) * kSlice2, last);                                                          \
-    __builtin_amdgcn_sched_barrier(0);                                                                   \
-    issue_stage2(ra, LA_NXT, a_off, kn, wid);                                                            \
-    issue_stage2(rb, LB_NXT, b_off, kn, wid);                                                            \
-    v4i fb[2][TJ];                                                                                       \
-    _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                        \
-      _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                                     \
-        fb[t][j] = *reinterpret_cast<const v4i*>(LB + b_rd[t] + j * 16 * kSlice2);                       \
-    _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                                     \
-      const v4i a0 = *reinterpret_cast<const v4i*>(LA + a_rd[0] + i * 16 * kSlice2);                    \
-      const v4i a1 = *reinterpret_cast<const v4i*>(LA + a_rd[1] + i * 16 * kSlice2);                    \
-      const v8i av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);                            \
-      _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                                   \
-        const v8i bv = __builtin_shufflevector(fb[0][j], fb[1][j], 0, 1, 2, 3, 4, 5, 6, 7);              \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 127, 0, 127); \
-      }                                                                                                  \
+    _Pragma("unroll") for (int i = 0; i + 1 < TI; ++i) {                                                 \
+      const v8i a_nxt = lds_frag8(LA + (i + 1) * 16 * kSlice2, a_rd[0], a_rd[1]);                        \
+      fp8_block(acc[i], a_cur, fb);                                                                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); /* the two LDS reads of block i+1 */            \
+      __builtin_amdgcn_sched_group_barrier(0x008, TJ, 0); /* then block i's MFMAs */                     \
+      a_cur = a_nxt;                                                                                     \
     }                                                                                                    \
+    fp8_block(acc[TI - 1], a_cur, fb);                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                                   \
+    __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0): stage s+1 landed, stage s reads done */ \
+    stage_barrier();                                                                                     \
+    const int kn = min((s + 2) * kSlice2, last);                                                          \
+    issue_stage2(ra, LA, a_off, kn, wid);                                                                \
+    issue_stage2(rb, LB, b_off, kn, wid);                                                                \
+    _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                                       \
+      fb[j] = lds_frag8(LB_NXT + j * 16 * kSlice2, b_rd[0], b_rd[1]);                                    \
+    a_cur = lds_frag8(LA_NXT, a_rd[0], a_rd[1]);                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                                   \
     ++s;                                                                                                 \
   }
   int s = 0;
