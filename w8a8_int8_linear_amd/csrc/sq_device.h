@@ -302,11 +302,15 @@ __device__ __forceinline__ float fp8_step(float amax) { return div_rn(amax, 448.
 
 // Per-row FP8 quantiser: code = E4M3(fl32(y / step)), round half to even
 // (v_cvt_pk_fp8_f32 rounds that way; gfx950 converts to OCP E4M3). As in
-// Quantizer, t = fl32(y * fl32(1 / step)) stands in for the quotient: the two
-// differ by under 2 binary32 ulps, so they round to the same E4M3 value unless
-// t lies within a few ulps of an E4M3 midpoint. For |t| >= 2^-6 a midpoint is
-// where the 20 bits below E4M3's 3-bit mantissa read 0x80000 (checked with an
-// 8-ulp margin); nonzero |t| < 2^-6 (E4M3's subnormal range) always divides.
+// Quantizer, t = fl32(y * fl32(1 / step)) stands in for the quotient q: with
+// |t| in [2^e, 2^(e+1)), |t - q| <= |q| 2^-23 (1 + 2^-25) is below 2.0001 ulps
+// of t, and below one ulp of t when q < 2^e, so q lies strictly between the
+// binary32 values 4 bit steps below and above t (the step below 2^e is half
+// as wide). E4M3 rounding is monotone: when those two neighbours get the same
+// code, q gets it too; otherwise (a midpoint lies between them, in E4M3's
+// normal or subnormal range alike) the codes come from exact quotients. The
+// step below saturates at +0 (a zero y keeps its zero code); below -0 it
+// wraps to a NaN pattern, which only sends those 8 values to the exact path.
 // |t| stays within 448 * (1 + 2^-23), below the 464 midpoint past which E4M3
 // has only NaN.
 struct QuantizerFp8 {
@@ -317,29 +321,30 @@ struct QuantizerFp8 {
     exact_only = st < 0x1p-100f;
     rcp = zero ? 0.0f : div_rn(1.0f, st);
   }
-  template <bool CLIP = false>
-  __device__ __forceinline__ uint2 codes8(const float y[8]) const {
-    static_assert(!CLIP, "FP8 codes use a step of their own row");
-    if (zero) return make_uint2(0u, 0u);                 // workgroup-uniform
-    float t[8];
-    bool slow = exact_only;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      t[i] = mul_rn(y[i], rcp);
-      const uint32_t u = __float_as_uint(t[i]) & 0x7fffffffu;
-      const bool sub = u != 0u && u < 0x3c800000u;                                 // 0 < |t| < 2^-6
-      const bool mid = (u & 0xfffffu) - 0x7fff8u <= 16u;                          // within 8 ulps of ...80000
-      slow |= sub | mid;
-    }
-    if (slow) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = div_rn(y[i], step);
-    }
+  __device__ __forceinline__ static uint2 pack8(const float t[8]) {
     int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w0, true);
     int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], 0, false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], w1, true);
     return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
+  }
+  template <bool CLIP = false>
+  __device__ __forceinline__ uint2 codes8(const float y[8]) const {
+    static_assert(!CLIP, "FP8 codes use a step of their own row");
+    if (zero) return make_uint2(0u, 0u);                 // workgroup-uniform
+    float lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = __float_as_uint(mul_rn(y[i], rcp));
+      lo[i] = __uint_as_float(__builtin_elementwise_sub_sat(u, 4u));
+      hi[i] = __uint_as_float(u + 4u);
+    }
+    const uint2 a = pack8(lo), b = pack8(hi);
+    if (!exact_only && a.x == b.x && a.y == b.y) return a;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = div_rn(y[i], step);
+    return pack8(t);
   }
 };
 
