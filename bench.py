@@ -398,13 +398,47 @@ def fp8_sweep(args):
 
 
 def summarize_fp8(trace_dir):
-    kernel_stats_table(
-        trace_dir, "INT8 against FP8 (OCP E4M3), MT-NLG-530B-width sites", FP8_CMD, "--summarize-fp8",
-        "Sites: LayerNorm 8192x20480 -> fc1 (N 81920) and NONE 8192x81920 -> fc2 (N 20480), fp16. "
-        "`k_norm_quant` mode 0 is the INT8 per-token quantiser and mode 3 the FP8 one; `k_gemm_tile` is the "
-        "INT8 GEMM (v_mfma_i32_16x16x64_i8) and `k_gemm_tile_fp8` the FP8 one "
-        "(v_mfma_scale_f32_16x16x128_f8f6f4); the fold's kernels are shared but for the weight quantiser.",
-        "kernel_stats_fp8_mtnlg530b.md")
+    """Per-dispatch durations of a --fp8 kernel trace, grouped by kernel and grid (one kernel name
+    serves both the activation quantiser and the fold's weight quantiser), as a profiles/ table."""
+    import csv
+    import glob
+    import statistics
+    hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    groups = {}
+    for r in csv.DictReader(open(hits[0])):
+        if "sq::" not in r["Kernel_Name"]:
+            continue
+        short = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        ms = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        groups.setdefault((short, wgs, r["Workgroup_Size_X"]), []).append(ms)
+    lines = ["# rocprofv3 kernel trace: INT8 against FP8 (OCP E4M3), MT-NLG-530B-width sites", "",
+             f"Command: `{FP8_CMD}`, then `python bench.py --summarize-fp8 <dir>`.", "",
+             "Sites: LayerNorm 8192x20480 -> fc1 (N 81920) and NONE 8192x81920 -> fc2 (N 20480), fp16. "
+             "`k_norm_quant` mode 0 is the INT8 per-token quantiser and mode 3 the FP8 one; with no norm the same "
+             "kernel quantises the fold's weights (81920x20480, 20480x81920); where one grid serves both, the "
+             "dispatches are split at their widest duration gap (the 20480-row weights take about 2.5x the "
+             "8192-row activations). "
+             "`k_gemm_tile` is the INT8 GEMM (v_mfma_i32_16x16x64_i8), `k_gemm_tile_fp8` the FP8 one "
+             "(v_mfma_scale_f32_16x16x128_f8f6f4). Durations are per dispatch, start to end.", "",
+             "| kernel | workgroups x threads | calls | median ms | min ms | max ms |",
+             "|---|---|---|---|---|---|"]
+    rows = []
+    for (name, wgs, wgsize), v in groups.items():
+        v = sorted(v)
+        # one kernel and grid may serve two row counts: split at the widest duration gap above 1.5x
+        # that leaves at least three dispatches on each side
+        ratio, cut = max(((v[i + 1] / v[i], i + 1) for i in range(2, len(v) - 3) if v[i] > 0), default=(1.0, 0))
+        parts = [v[:cut], v[cut:]] if ratio > 1.5 else [v]
+        rows += [(name, wgs, wgsize, p) for p in parts]
+    for name, wgs, wgsize, v in sorted(rows, key=lambda r: (-statistics.median(r[3]), r[0])):
+        lines.append(f"| `{name}` | {wgs} x {wgsize} | {len(v)} | {statistics.median(v):.4f} | "
+                     f"{min(v):.4f} | {max(v):.4f} |")
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_fp8_mtnlg530b.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 # ----------------------------------------------------------------------------- accuracy study
