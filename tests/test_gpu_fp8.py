@@ -227,7 +227,10 @@ def test_fp8_mfma_group_truncation():
 
 
 GEMM_SHAPES = [(17, 33, 128), (256, 256, 128), (300, 520, 384), (513, 700, 1280), (64, 16416, 2176),
-               (1024, 2048, 20480), (5, 9, 133120)]
+               (1024, 2048, 20480), (5, 9, 133120),
+               # decode (M <= 64): every token-tile count, narrow and 144-channel strips, ragged N
+               (1, 9216, 9216), (2, 1000, 1280), (4, 36864, 9216), (16, 130, 384), (33, 4000, 2048),
+               (48, 16400, 1024), (64, 36864, 9216), (65, 300, 256)]
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))

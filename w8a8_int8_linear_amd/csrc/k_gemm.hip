@@ -651,11 +651,17 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 // serves NT weight tiles). The four waves split each segment as (K step
 // = wave & 1, channel-tile half = wave >> 1); the two K steps' partials are
 // summed through LDS at the end. Segments go through an R-stage ring.
+//
+// FP8 (E4M3 codes, K % 128 == 0): one v_mfma_scale_f32_16x16x128_f8f6f4 takes a
+// whole segment (K bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of a row for
+// lane group g, as in the prefill kernel), so the wave pairs split the
+// segments by parity instead of the K steps, into binary32 accumulators, and
+// the two partials meet through LDS the same way.
 constexpr int kDecNowhere = 0x40000000;               // a buffer offset past every operand: loads return zeros
 constexpr int kDec2Seg = 128;
 constexpr int kDec2Tile = 16 * kDec2Seg;             // LDS bytes of one 16-row operand tile
 
-template <int NT, int MT, int R, int YDT>
+template <int NT, int MT, int R, int YDT, bool FP8 = false>
 __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __restrict__ xq,
                                                                 const float* __restrict__ xs,
                                                                 const int8_t* __restrict__ wq,
@@ -726,15 +732,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
     }
   };
 
-  // compute share: K step t of each segment, channel tiles [h NH, h NH + NH) (clipped to NT)
+  // compute share: K step t of each segment (FP8: the segments of parity t),
+  // channel tiles [h NH, h NH + NH) (clipped to NT)
+  using AccV = std::conditional_t<FP8, v4f, v4i>;
   const int t = wid & 1, h = wid >> 1;
   const int c = 4 * t + (lane >> 4), r16 = lane & 15;
   const int frag = r16 * kDec2Seg + 16 * (c ^ swz2(r16));
-  v4i acc[NH][MT];
+  const int frag_lo = r16 * kDec2Seg + 16 * ((lane >> 4) ^ swz2(r16));          // FP8: both chunks of lane group g
+  const int frag_hi = r16 * kDec2Seg + 16 * ((4 + (lane >> 4)) ^ swz2(r16));
+  AccV acc[NH][MT];
 #pragma unroll
   for (int j = 0; j < NH; ++j)
 #pragma unroll
-    for (int u = 0; u < MT; ++u) acc[j][u] = v4i{0, 0, 0, 0};
+    for (int u = 0; u < MT; ++u) acc[j][u] = AccV{0, 0, 0, 0};
 
 #define SQ_DEC_PRO(I) \
   if constexpr (I < R - 1) { issue(std::integral_constant<int, I>{}, I); memory_opaque(); }
@@ -746,7 +756,35 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * kPerWave));
     stage_barrier();
     issue(std::integral_constant<int, (kk + R - 1) % R>{}, seg + R - 1);
-    if (2 * seg + t < steps) {
+    if constexpr (FP8) {
+      if ((seg & 1) == t) {
+        const uint32_t b = lds_addr(stage(k));
+        uint32_t addr[2 * (NH + MT)];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const uint32_t tb = b + min(h * NH + j, NT - 1) * kDec2Tile;
+          addr[2 * j] = tb + frag_lo;
+          addr[2 * j + 1] = tb + frag_hi;
+        }
+#pragma unroll
+        for (int u = 0; u < MT; ++u) {
+          const uint32_t tb = b + (NT + u) * kDec2Tile;
+          addr[2 * (NH + u)] = tb + frag_lo;
+          addr[2 * (NH + u) + 1] = tb + frag_hi;
+        }
+        v4i f[2 * (NH + MT)];
+        lds_read_frags(f, addr);
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const v8i fw = __builtin_shufflevector(f[2 * j], f[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int u = 0; u < MT; ++u) {
+            const v8i fx = __builtin_shufflevector(f[2 * (NH + u)], f[2 * (NH + u) + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[j][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw, fx, acc[j][u], 0, 0, 0, 127, 0, 127);
+          }
+        }
+      }
+    } else if (2 * seg + t < steps) {
       const uint32_t base = lds_addr(stage(k)) + frag;
       uint32_t addr[NH + MT];
 #pragma unroll
@@ -782,7 +820,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
 #pragma unroll
     for (int j = 0; j < NH; ++j)
 #pragma unroll
-      for (int u = 0; u < MT; ++u) reinterpret_cast<v4i*>(park)[(j * MT + u) * 64 + lane] = acc[j][u];
+      for (int u = 0; u < MT; ++u) reinterpret_cast<AccV*>(park)[(j * MT + u) * 64 + lane] = acc[j][u];
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   stage_barrier();
@@ -792,7 +830,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
     if (h * NH + j >= NT) continue;                              // uniform
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
-      const v4i v = acc[j][u] + reinterpret_cast<const v4i*>(park)[(j * MT + u) * 64 + lane];
+      const AccV v = acc[j][u] + reinterpret_cast<const AccV*>(park)[(j * MT + u) * 64 + lane];
       const int m = 16 * u + (lane & 15);
       const int n = n0 + 16 * (h * NH + j) + 4 * (lane >> 4);
       if (m < M && n < N) store4<YDT>(y, N, m, n, v, (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
@@ -903,40 +941,47 @@ __global__ __launch_bounds__(256) void k_gemv(const int8_t* __restrict__ xq, con
 
 namespace {
 
-template <int YDT>
-hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64) {
-    // Up to 4 tokens: the vector-ALU GEMV, 16 channels per workgroup. More:
-    // the MFMA decode kernel with up to 9 channel tiles per workgroup, so that
-    // each token segment serves many weight tiles (fewer at small N, to keep
-    // every CU busy). Measured on K = 9216, N = 9216 / 36864.
-    const int mt = (g.M + 15) / 16;
-    const bool wide = g.N >= 16384;
+// Decode shapes (M <= 64). INT8 with up to 4 tokens: the vector-ALU GEMV, 16
+// channels per workgroup (gfx950 has no FP8 dot product on the vector ALUs, so
+// FP8 always takes the MFMA kernel). Otherwise the MFMA decode kernel with up
+// to 9 channel tiles per workgroup, so that each token segment serves many
+// weight tiles (fewer at small N, to keep every CU busy). Measured on
+// K = 9216, N = 9216 / 36864.
+template <int YDT, bool FP8>
+hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
+  const int mt = (g.M + 15) / 16;
+  const bool wide = g.N >= 16384;
 #define SQ_DECODE(KERN, CH)                                                                                  \
   {                                                                                                          \
     hipLaunchKernelGGL(KERN, dim3((g.N + (CH) - 1) / (CH)), dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale,   \
                        g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
     return hipGetLastError();                                                                                \
   }
+  if constexpr (!FP8) {
     if (g.M == 1) SQ_DECODE((k_gemv<1, 3, YDT>), 16)
     if (g.M == 2) SQ_DECODE((k_gemv<2, 3, YDT>), 16)
     if (g.M <= 4) SQ_DECODE((k_gemv<4, 2, YDT>), 16)
-    if (mt == 1) {
-      if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT>), 144)
-      SQ_DECODE((k_gemm_decode<4, 1, 7, YDT>), 64)
-    }
-    if (mt == 2) {
-      if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT>), 144)
-      SQ_DECODE((k_gemm_decode<4, 2, 6, YDT>), 64)
-    }
-    if (mt == 3) {
-      if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT>), 144)
-      SQ_DECODE((k_gemm_decode<3, 3, 5, YDT>), 48)
-    }
-    if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT>), 144)
-    SQ_DECODE((k_gemm_decode<3, 4, 5, YDT>), 48)
-#undef SQ_DECODE
   }
+  if (mt == 1) {
+    if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT, FP8>), 144)
+    SQ_DECODE((k_gemm_decode<4, 1, 7, YDT, FP8>), 64)
+  }
+  if (mt == 2) {
+    if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT, FP8>), 144)
+    SQ_DECODE((k_gemm_decode<4, 2, 6, YDT, FP8>), 64)
+  }
+  if (mt == 3) {
+    if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT, FP8>), 144)
+    SQ_DECODE((k_gemm_decode<3, 3, 5, YDT, FP8>), 48)
+  }
+  if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT, FP8>), 144)
+  SQ_DECODE((k_gemm_decode<3, 4, 5, YDT, FP8>), 48)
+#undef SQ_DECODE
+}
+
+template <int YDT>
+hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 64) return launch_decode<YDT, false>(g, st);
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
@@ -953,6 +998,7 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
 
 template <int YDT>
 hipError_t launch_fp8_typed(const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 64) return launch_decode<YDT, true>(g, st);
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
