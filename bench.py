@@ -56,7 +56,8 @@ def parse():
     p.add_argument("--summarize-granularities", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --granularities into a profiles/ table and exit")
     p.add_argument("--fp8", action="store_true",
-                   help="INT8 against FP8 (E4M3) per stage on the MT-NLG-530B-width sites (HIP-event medians) and exit")
+                   help="INT8 against FP8 (E4M3) per stage on the MT-NLG-530B-width sites (HIP-event medians) and "
+                        "exit; with --decode-sweep / --summarize-decode, the FP8 decode GEMMs instead")
     p.add_argument("--summarize-fp8", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --fp8 into a profiles/ table and exit")
     return p.parse_args()
@@ -181,44 +182,53 @@ def decode_bytes(m, n, k=DEC_K):
     return n * k + m * k + 4 * (m + n) + 2 * m * n
 
 
-def decode_sweep():
+def decode_sweep(fp8=False):
     """Decode GEMMs at the OPT-66B width with enough weight copies (>= 600 MB) rotating that no
     launch finds its weights in the 256 MB MALL; HIP-event medians per shape (the launch gap
-    included; the rocprofv3 trace of this run gives the kernel durations)."""
+    included; the rocprofv3 trace of this run gives the kernel durations). fp8: E4M3 codes of
+    N(0, 1) values through sq_fp8_gemm instead of INT8 codes through sq_w8a8_gemm."""
     import torch
     import w8a8_int8_linear_amd as sq
     gen = torch.Generator(device="cpu").manual_seed(3)
+
+    def codes(rows):
+        if fp8:
+            return torch.randn(rows, DEC_K, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+        return torch.randint(-127, 128, (rows, DEC_K), dtype=torch.int8, generator=gen).cuda()
+
+    gemm = sq.sq_fp8_gemm if fp8 else sq.sq_w8a8_gemm
     for n in DEC_NS:
         copies = max(2, -(-600_000_000 // (n * DEC_K)))
-        ws = [torch.randint(-127, 128, (n, DEC_K), dtype=torch.int8, generator=gen).cuda() for _ in range(copies)]
+        ws = [codes(n) for _ in range(copies)]
         wsc = (torch.rand(n, generator=gen) * 0.01).cuda()
         for m in DEC_MS:
-            xq = torch.randint(-127, 128, (m, DEC_K), dtype=torch.int8, generator=gen).cuda()
+            xq = codes(m)
             xs = (torch.rand(m, generator=gen) * 0.01).cuda()
             y = torch.empty(m, n, dtype=torch.float16, device="cuda")
             for i in range(DEC_WARM):
-                sq.sq_w8a8_gemm(xq, xs, ws[i % copies], wsc, y=y, out_dtype=torch.float16)
+                gemm(xq, xs, ws[i % copies], wsc, y=y, out_dtype=torch.float16)
             torch.cuda.synchronize()
             ts = []
             for i in range(DEC_ITERS):
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
-                sq.sq_w8a8_gemm(xq, xs, ws[i % copies], wsc, y=y, out_dtype=torch.float16)
+                gemm(xq, xs, ws[i % copies], wsc, y=y, out_dtype=torch.float16)
                 b.record()
                 torch.cuda.synchronize()
                 ts.append(a.elapsed_time(b) * 1e3)
             ts.sort()
             med = ts[len(ts) // 2]
-            print(json.dumps({"decode": [m, n, DEC_K], "us_event_median": round(med, 2),
+            print(json.dumps({"decode": [m, n, DEC_K], "format": "fp8" if fp8 else "int8", "us_event_median": round(med, 2),
                               "GBps": round(decode_bytes(m, n) / med / 1e3, 1)}), flush=True)
             del xq, y
         del ws
         torch.cuda.empty_cache()
 
 
-def summarize_decode(trace_dir):
-    """Kernel durations of a --decode-sweep trace, matched to its shapes by dispatch order."""
+def summarize_decode(trace_dir, fp8=False):
+    """Kernel durations of a --decode-sweep trace (with --fp8: of --decode-sweep --fp8), matched to
+    its shapes by dispatch order."""
     import csv
     import glob
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
@@ -230,8 +240,9 @@ def summarize_decode(trace_dir):
     shapes = [(m, n) for n in DEC_NS for m in DEC_MS]
     if len(rows) != per * len(shapes):
         raise SystemExit(f"expected {per * len(shapes)} dispatches, found {len(rows)}")
-    lines = ["# Decode GEMM kernel durations (rocprofv3 kernel trace): OPT-66B width, K = 9216, fp16 out", "",
-             f"Command: `{DEC_CMD}`, then `python bench.py --summarize-decode <dir>`.", "",
+    fmt, flag = ("FP8 (E4M3)", " --fp8") if fp8 else ("INT8", "")
+    lines = [f"# {fmt} decode GEMM kernel durations (rocprofv3 kernel trace): OPT-66B width, K = 9216, fp16 out", "",
+             f"Command: `{DEC_CMD}{flag}`, then `python bench.py --summarize-decode <dir>{flag}`.", "",
              "Each shape: 2 warm-up and 12 timed launches, rotating weight copies totalling >= 600 MB so that "
              "no launch finds its weights in the MALL. Bytes = Wq + Xq + scales + fp16 output; "
              "the bar is 75% of 8 TB/s.", "",
@@ -243,7 +254,8 @@ def summarize_decode(trace_dir):
         name = rs[0]["Kernel_Name"].split("(")[0].replace("void ", "")
         b = decode_bytes(m, n)
         lines.append(f"| {m} | {n} | `{name}` | {med:.2f} | {du[0]:.2f} | {b / med / 1e6:.2f} | {b / 6e6:.2f} |")
-    with open(os.path.join(ROOT, "profiles", "decode_gemm_opt66b_k9216.md"), "w") as f:
+    out = "decode_gemm_fp8_opt66b_k9216.md" if fp8 else "decode_gemm_opt66b_k9216.md"
+    with open(os.path.join(ROOT, "profiles", out), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -664,7 +676,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.summarize_decode:
-        summarize_decode(args.summarize_decode)
+        summarize_decode(args.summarize_decode, args.fp8)
         return
     if args.summarize_granularities:
         summarize_granularities(args.summarize_granularities)
@@ -677,7 +689,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.decode_sweep:
-        decode_sweep()
+        decode_sweep(args.fp8)
         return
     if args.granularities:
         granularity_sweep(args)
