@@ -9,7 +9,9 @@ single-GPU prefill configuration.
 
 Prints one JSON line. `value` is the step's GEMM work (2*M*N*K summed over the
 sites) divided by the step time, in TOPS; `roofline` reports the GEMM kernel
-against the INT8 dense MFMA peak from HIP events around each launch; `kernels`
+against the INT8 dense MFMA peak from HIP events around each launch (with the
+HBM traffic, shader clock and MFMA-busy fraction of the committed rocprofv3
+counter record while the GEMM sources are unchanged since it was taken); `kernels`
 gives every stage's average duration and its achieved rate; `cpu_baseline` times
 the CPU oracle on a bounded sample of the same workload.
 """
@@ -40,7 +42,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration runs)")
-    p.add_argument("--summarize-counters", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="turn rocprofv3 CSV output of this benchmark into profiles/ summaries and exit")
     p.add_argument("--decode-sweep", action="store_true",
                    help="time the decode GEMMs (K=9216, N in {9216, 36864}, 1..64 tokens) with rotating weight "
@@ -93,11 +95,41 @@ def recorded_traffic():
     return rec
 
 
-def summarize_counters(trace_dir, fetch_dir, write_dir):
+N_XCD, N_CU, SIMD_PER_CU, PEAK_SCLK_GHZ = 8, 256, 4, 2.4     # MI355X; the dense peaks are quoted at 2.4 GHz
+
+
+def gemm_clock(clock_dir):
+    """Shader clock and MFMA-busy fraction of each GEMM dispatch of a --pmc GRBM_GUI_ACTIVE
+    SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES run: GRBM_GUI_ACTIVE sums the busy cycles of the
+    XCDs, so cycles per XCD over the dispatch's duration is the clock; the MFMA busy cycles,
+    summed over the CUs, are divided by the cycles of every SIMD."""
+    import csv
+    import glob
+    from collections import defaultdict
+    hits = glob.glob(os.path.join(clock_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no counter collection under {clock_dir}")
+    per = defaultdict(dict)
+    for r in csv.DictReader(open(hits[0])):
+        if "k_gemm_tile" in r["Kernel_Name"]:
+            d = per[int(r["Dispatch_Id"])]
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = []
+    for _, d in sorted(per.items()):
+        cyc = d["GRBM_GUI_ACTIVE"] / N_XCD
+        out.append({"ms": d["ns"] / 1e6, "sclk_GHz": cyc / d["ns"],
+                    "mfma_busy": d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_CU * SIMD_PER_CU) / cyc})
+    return out
+
+
+def summarize_counters(trace_dir, fetch_dir, write_dir, clock_dir=None):
     """rocprofv3 CSVs of `bench.py` runs -> profiles/*.md and the GEMM traffic record.
 
     FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what it reads for
     the plain device copy of --copy-probe-mib MiB that the counter runs add at the end.
+    With clock_dir (a GRBM_GUI_ACTIVE / MFMA-busy run), the record also carries each GEMM
+    dispatch's shader clock and MFMA-busy fraction.
     """
     import csv
     import glob
@@ -133,11 +165,20 @@ def summarize_counters(trace_dir, fetch_dir, write_dir):
                  "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline")
     cmd_pmc = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o run --output-format csv -- "
                "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-probe-mib 1024")
+    cmd_clock = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES -d <dir> -o run "
+                 "--output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline")
     rec = {"kernel": "k_gemm_tile", "workload": "mtnlg530b_width_m8192_h20480 (fc1 then fc2)",
            "source_sha256": gemm_source_hash(), "fetch_scale": scale["FETCH_SIZE"],
            "write_scale": scale["WRITE_SIZE"], "launches": launches,
            "traffic_bytes_per_launch": sum(l["fetch_bytes"] + l["write_bytes"] for l in launches) / len(launches),
            "commands": [cmd_trace, cmd_pmc]}
+    if clock_dir:
+        clk = gemm_clock(clock_dir)
+        timed = clk[-2:]                                 # the timed step's fc1 and fc2; the rest warm up
+        rec["clock"] = clk
+        rec["sclk_GHz"] = sum(c["sclk_GHz"] for c in timed) / len(timed)
+        rec["mfma_busy"] = sum(c["mfma_busy"] for c in timed) / len(timed)
+        rec["commands"].append(cmd_clock)
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(rec, f, indent=1)
@@ -165,6 +206,25 @@ def summarize_counters(trace_dir, fetch_dir, write_dir):
         lines.append(f"| {fd} | `{name.split('(')[0].replace('void ', '')}` | {fb:.3f} | {wb:.3f} |")
     with open(os.path.join(ROOT, "profiles", "hbm_traffic_mtnlg530b_width.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    if clock_dir:
+        lines = ["# Shader clock and MFMA busy of the GEMM (rocprofv3 counters): MT-NLG-530B-width layer", "",
+                 f"Command: `{cmd_clock}`.", "",
+                 "One warm-up step, then the timed step; the bench reports the timed step's averages "
+                 f"(clock {rec['sclk_GHz']:.3f} GHz, MFMA busy {rec['mfma_busy']:.3f}).", "",
+                 f"Clock = GRBM_GUI_ACTIVE / {N_XCD} XCDs / dispatch duration; MFMA busy = "
+                 f"SQ_VALU_MFMA_BUSY_CYCLES / ({N_CU} CUs x {SIMD_PER_CU} SIMDs) / cycles per XCD. The dense INT8 "
+                 f"peak of 5.0 POPS is quoted at {PEAK_SCLK_GHZ} GHz and scales with the clock.", "",
+                 "| dispatch | ms | shader clock GHz | MFMA busy | TOPS | peak at this clock | fraction of it |",
+                 "|---|---|---|---|---|---|---|"]
+        n_clk = len(rec["clock"])
+        for i, c in enumerate(rec["clock"]):
+            tops = 2.0 * 8192 * 81920 * 20480 / (c["ms"] * 1e-3) / 1e12
+            pk = PEAK_INT8_TOPS * c["sclk_GHz"] / PEAK_SCLK_GHZ
+            tag = ("fc1" if i % 2 == 0 else "fc2") + (" (warm-up)" if i < n_clk - 2 else "")
+            lines.append(f"| {tag} | {c['ms']:.3f} | {c['sclk_GHz']:.3f} | "
+                         f"{c['mfma_busy']:.3f} | {tops:.0f} | {pk:.0f} | {tops / pk:.3f} |")
+        with open(os.path.join(ROOT, "profiles", "gemm_clock_mtnlg530b_width.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
     print(json.dumps(rec, indent=1))
 
 
@@ -673,6 +733,8 @@ def cpu_baseline(wl, budget_s):
 def main():
     args = parse()
     if args.summarize_counters:
+        if len(args.summarize_counters) not in (3, 4):
+            raise SystemExit("--summarize-counters TRACE_DIR FETCH_DIR WRITE_DIR [CLOCK_DIR]")
         summarize_counters(*args.summarize_counters)
         return
     if args.summarize_decode:
@@ -738,6 +800,8 @@ def main():
     alg_bytes = [d["n"] * d["k"] + 4 * d["n"] + d["m"] * d["k"] + 4 * d["m"] + osize * d["m"] * d["n"] for d in sites]
     rec = recorded_traffic() if args.workload == 5 and m == 8192 else None
     traffic = rec["traffic_bytes_per_launch"] if rec else None
+    sclk = rec.get("sclk_GHz") if rec else None
+    peak_sclk = PEAK_INT8_TOPS * sclk / PEAK_SCLK_GHZ if sclk else None
     out = {
         "metric": "W8A8 GEMM TOPS + % INT8 MFMA peak; norm+quant kernel HBM GB/s",
         "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -749,6 +813,10 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_gemm_tile", "achieved": round(achieved, 1),
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch",
+                     "sclk_GHz": round(sclk, 3) if sclk else None,
+                     "peak_at_sclk": round(peak_sclk, 1) if sclk else None,
+                     "frac_at_sclk": round(achieved / peak_sclk, 4) if sclk else None,
+                     "mfma_busy": round(rec["mfma_busy"], 3) if rec and "mfma_busy" in rec else None,
                      "algorithmic_bytes_per_launch": sum(alg_bytes) / len(alg_bytes),
                      "ops_per_launch": sum(g_ops) / len(g_ops)},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
