@@ -726,8 +726,15 @@ def cpu_baseline(wl, budget_s):
             break
     sample = (f"{reps} x every site's full oracle chain on {m_s} tokens, {cal_s} calibration tokens and the first "
               f"{n_s} output channels at full K")
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": ops / elapsed / 1e12, "unit": "TOPS", "cores": int(blas), "kind": "oracle", "sample": sample,
-            "seconds": elapsed, "note": "numpy, single-threaded except the BLAS matrix product"}
+            "seconds": elapsed, "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "note": "numpy, single-threaded except the BLAS matrix product"}
 
 
 def main():
