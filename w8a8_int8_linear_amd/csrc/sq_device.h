@@ -43,8 +43,6 @@ template <> struct Storage<f32_t> { static constexpr int kBytes = 4; };
 template <> struct Storage<f16_t> { static constexpr int kBytes = 2; };
 template <> struct Storage<bf16_t> { static constexpr int kBytes = 2; };
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }
