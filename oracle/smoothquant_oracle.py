@@ -49,8 +49,10 @@ R14 per-tensor granularity ("SmoothQuant, in depth", "Granularity: O1, O2, O3":
     clip, as the page's failure-mode note on static scales says). The per-row
     and per-channel scale vectors the GEMM reads hold the step repeated, so
     R6 is unchanged.
-R16 the FP8 variant ("LLM.int8() and SmoothQuant", "In papers" / "INT8,
-    Everywhere" on the move to FP8): codes are OCP E4M3 (bias 7, 3 mantissa
+R16 the FP8 variant ("SmoothQuant -- interactive paper explainer", timeline
+    "2023+ The efficiency stack" and "What it did NOT solve"; "LLM.int8() and
+    SmoothQuant", "example: what you get": FP8 W8A8 took over the INT8 role and
+    kept the smoothing): codes are OCP E4M3 (bias 7, 3 mantissa
     bits, largest finite 448, no infinities, S.1111.111 is NaN); a per-row step
     is fl32(absmax / 448) and a code is the round-half-even E4M3 value of
     fl32(v / step). Magnitudes above 448 round to NaN past the 464 midpoint
@@ -61,6 +63,11 @@ R16 the FP8 variant ("LLM.int8() and SmoothQuant", "In papers" / "INT8,
 R15 the static activation step is fl32(max_j fl32(a_j / s_j) / 127): the
     smoothed input of channel j is y_j / s_j, so its calibration maximum is
     a_j / s_j (a_j from R5, s_j from R4).
+R18 FP8 with one step for the whole tensor (R14's granularities with R16's
+    codes): the dynamic step is fl32(max |y| / 448), the static one
+    fl32(max_j fl32(a_j / s_j) / 448) (R15), and the quotient fl32(v / step) is
+    saturated to [-448, 448] before encoding, as INT8 codes clip to +-127: a
+    value beyond the step's range takes the largest code, never NaN.
 
 Where a step rounds a real number that the oracle computes exactly (R2, R4),
 it also reports how far that number lies from the binary32 rounding boundary,
@@ -84,7 +91,8 @@ __all__ = [
     "int_gemm", "int_gemm_loops", "dequantize", "w8a8_linear",
     "quantize_tensor", "norm_quant_per_tensor", "static_step", "fold_per_tensor",
     "E4M3_MAX", "e4m3_encode", "e4m3_decode", "quantize_rows_fp8", "norm_quant_fp8", "fold_fp8", "gemm_fp8",
-    "gemm_fp8_bound",
+    "gemm_fp8_bound", "quantize_tensor_fp8", "norm_quant_fp8_per_tensor", "static_step_fp8",
+    "fold_fp8_per_tensor",
 ]
 
 F32 = np.float32
@@ -518,6 +526,57 @@ def gemm_fp8_bound(xq, wq, k_step: int = 128) -> np.ndarray:
     k = a.shape[1]
     n = -(-k // k_step) + int(math.log2(k_step)) + 2
     return n * 2.0 ** -24 * (a @ b.T)
+
+
+def quantize_tensor_fp8(y, step=None):
+    """One FP8 step for a whole tensor (reading R18).
+
+    step None: the dynamic step fl32(max |y| / 448) over every element; otherwise
+    the given static step. Codes are E4M3(clip(fl32(y / step), -448, 448)), the
+    clip saturating values beyond the step's range; a step that is not positive
+    gives all-zero codes. Returns (codes uint8, step fp32 scalar).
+    """
+    y = np.atleast_2d(np.asarray(y, dtype=F32))
+    if step is None:
+        amax = np.max(np.abs(y)) if y.size else F32(0)
+        step = F32(amax) / F32(E4M3_MAX)
+    step = F32(step)
+    if not step > 0:
+        return np.zeros(y.shape, np.uint8), step
+    with np.errstate(over="ignore"):
+        t = (y / step).astype(F32)
+    t = np.clip(t, F32(-E4M3_MAX), F32(E4M3_MAX))
+    return e4m3_encode(t), step
+
+
+def norm_quant_fp8_per_tensor(x, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5, step=None):
+    """norm_quant_per_tensor with FP8 codes: one dynamic (step None) or static step for the tensor."""
+    x32 = widen(x, dtype)
+    if norm == NONE:
+        y = normalize(x32, NONE, gamma=gamma_f)
+        info = {"near_tie": np.zeros(x32.shape[0], bool), "alt": {}}
+    else:
+        mu, var, tie, alt = _stats_block(x32, norm)
+        y = normalize(x32, norm, mu, var, gamma_f, beta_f, eps)
+        info = {"mu": mu, "var": var, "near_tie": tie, "alt": alt}
+    q, st = quantize_tensor_fp8(y, step)
+    info["y"] = y
+    return q, np.full(x32.shape[0], st, F32), info
+
+
+def static_step_fp8(act_absmax, s):
+    """Static per-tensor FP8 activation step (reading R18): fl32(max_j fl32(a_j / s_j) / 448)."""
+    r = np.asarray(act_absmax, F32) / np.asarray(s, F32)
+    return F32(np.max(r) if r.size else F32(0)) / F32(E4M3_MAX)
+
+
+def fold_fp8_per_tensor(act_absmax, w, dtype, alpha, eps=EPS_FOLD, norm=NONE, gamma=None, beta=None, s=None):
+    """fold() with FP8 weight codes and one step fl32(max |W-hat| / 448) for the whole W-hat (R18)."""
+    f = fold(act_absmax, w, dtype, alpha, eps, norm, gamma, beta, s)
+    wq, st = quantize_tensor_fp8(f["w_hat"])
+    f["wq"] = wq
+    f["w_scale"] = np.full(f["w_hat"].shape[0], st, F32)
+    return f
 
 
 # --------------------------------------------------------------------------- O4 GEMM and epilogue
