@@ -258,6 +258,39 @@ sq_status sq_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq
                       const float* bias, void* y, sq_dtype y_dt,
                       int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * FP8 with one step for the whole tensor: the per-tensor granularities above
+ * ("SmoothQuant, in depth", "Granularity: O1, O2, O3 and what kernels run
+ * today") with E4M3 codes. Steps divide by 448 where the INT8 ones divide by
+ * 127, and the quotient fl32(v / step) is saturated to [-448, 448] before
+ * encoding (a value beyond a static step's range takes the largest code, never
+ * NaN). Arguments, layouts and errors as for the INT8 calls of the same name
+ * without _fp8; code buffers hold uint8 E4M3 bytes.
+ *
+ * sq_norm_quant_fp8_per_tensor: dynamic step fl32(max |y| / 448) over the
+ *   whole tensor (two passes over x); x_scale [M] receives it in every entry.
+ */
+sq_status sq_norm_quant_fp8_per_tensor(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                       sq_norm norm, const float* gamma_f, const float* beta_f, float eps,
+                                       uint8_t* xq, float* x_scale, void* stream);
+
+/* sq_norm_quant_fp8_static: the static step *step (device fp32, e.g. from
+ * sq_static_step_fp8); x_scale [M] receives it in every entry. */
+sq_status sq_norm_quant_fp8_static(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                   sq_norm norm, const float* gamma_f, const float* beta_f, float eps,
+                                   const float* step, uint8_t* xq, float* x_scale, void* stream);
+
+/* sq_static_step_fp8: *step = fl32(max_j fl32(act_absmax[j] / s[j]) / 448). */
+sq_status sq_static_step_fp8(const float* act_absmax, const float* s, int64_t K, float* step, void* stream);
+
+/* smoothquant_fold_fp8_per_tensor: smoothquant_fold_fp8 with one weight step
+ * fl32(max |W-hat| / 448) for the whole W-hat, repeated in w_scale [N]. */
+sq_status smoothquant_fold_fp8_per_tensor(const float* act_absmax, const void* w, sq_dtype w_dt,
+                                          int64_t N, int64_t K, double alpha, float eps,
+                                          sq_norm norm, const float* gamma, const float* beta,
+                                          float* s_out, float* gamma_out, float* beta_out,
+                                          uint8_t* wq, float* w_scale, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* sq_status_string(sq_status s);
 

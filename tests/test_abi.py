@@ -24,7 +24,8 @@ def test_header_declares_the_calls():
     assert _declared() == {"smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
                            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step",
                            "smoothquant_fold_per_tensor", "sq_norm_quant_fp8", "smoothquant_fold_fp8",
-                           "sq_fp8_gemm", "sq_status_string"}
+                           "sq_fp8_gemm", "sq_norm_quant_fp8_per_tensor", "sq_norm_quant_fp8_static",
+                           "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor", "sq_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -89,7 +90,33 @@ def fold8(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=No
     return L.smoothquant_fold_fp8(a, w, dt, n, k, ctypes.c_double(alpha), F(eps), norm, g, b, s, go, bo, wq, ws, None)
 
 
+def nq8t(x=A, dt=1, m=16, k=512, norm=0, g=None, b=None, eps=1e-5, xq=A, xs=A):
+    return L.sq_norm_quant_fp8_per_tensor(x, dt, m, k, norm, g, b, F(eps), xq, xs, None)
+
+
+def nq8s(x=A, dt=1, m=16, k=512, norm=0, g=None, b=None, eps=1e-5, step=A, xq=A, xs=A):
+    return L.sq_norm_quant_fp8_static(x, dt, m, k, norm, g, b, F(eps), step, xq, xs, None)
+
+
+def sstep8(a=A, s=A, k=512, step=A):
+    return L.sq_static_step_fp8(a, s, k, step, None)
+
+
+def fold8t(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=None, s=A, go=A, bo=None,
+           wq=A, ws=A):
+    return L.smoothquant_fold_fp8_per_tensor(a, w, dt, n, k, ctypes.c_double(alpha), F(eps), norm, g, b, s, go, bo,
+                                             wq, ws, None)
+
+
 @pytest.mark.parametrize("call,code", [
+    (lambda: nq8t(x=None), 1), (lambda: nq8t(xs=None), 1), (lambda: nq8t(dt=3), 2), (lambda: nq8t(k=100), 3),
+    (lambda: nq8t(xq=A4), 4), (lambda: nq8t(norm=0, b=A), 5), (lambda: nq8t(norm=1, eps=0.0), 5),
+    (lambda: nq8s(step=None), 1), (lambda: nq8s(x=None), 1), (lambda: nq8s(dt=7), 2), (lambda: nq8s(m=0), 3),
+    (lambda: nq8s(step=ctypes.c_void_p((1 << 20) + 2)), 4), (lambda: nq8s(norm=2, b=A), 5),
+    (lambda: sstep8(a=None), 1), (lambda: sstep8(step=None), 1), (lambda: sstep8(k=0), 3), (lambda: sstep8(k=100), 3),
+    (lambda: sstep8(s=ctypes.c_void_p((1 << 20) + 2)), 4),
+    (lambda: fold8t(a=None), 1), (lambda: fold8t(wq=None), 1), (lambda: fold8t(dt=3), 2), (lambda: fold8t(n=0), 3),
+    (lambda: fold8t(alpha=1.5), 5), (lambda: fold8t(w=A4), 4),
     (lambda: g8(ydt=3), 2), (lambda: g8(ydt=9), 2), (lambda: g8(k=192), 3), (lambda: g8(k=64), 3),
     (lambda: g8(xq=None), 1), (lambda: g8(xs=None), 1), (lambda: g8(m=0), 3), (lambda: g8(y=A4), 4),
     (lambda: nq8(x=None), 1), (lambda: nq8(dt=3), 2), (lambda: nq8(k=100), 3), (lambda: nq8(norm=0, b=A), 5),

@@ -19,13 +19,17 @@ from ._lib import (  # noqa: F401
     smoothquant_calibrate,
     smoothquant_fold,
     smoothquant_fold_fp8,
+    smoothquant_fold_fp8_per_tensor,
     smoothquant_fold_per_tensor,
     sq_fp8_gemm,
     sq_norm_quant,
     sq_norm_quant_fp8,
+    sq_norm_quant_fp8_per_tensor,
+    sq_norm_quant_fp8_static,
     sq_norm_quant_per_tensor,
     sq_norm_quant_static,
     sq_static_step,
+    sq_static_step_fp8,
     sq_w8a8_gemm,
     status_string,
 )

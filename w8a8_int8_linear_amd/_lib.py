@@ -26,7 +26,8 @@ _NORM = {"none": SQ_NORM_NONE, "layernorm": SQ_NORM_LAYERNORM, "rmsnorm": SQ_NOR
 
 EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step", "smoothquant_fold_per_tensor",
-           "sq_norm_quant_fp8", "smoothquant_fold_fp8", "sq_fp8_gemm", "sq_status_string")
+           "sq_norm_quant_fp8", "smoothquant_fold_fp8", "sq_fp8_gemm", "sq_norm_quant_fp8_per_tensor",
+           "sq_norm_quant_fp8_static", "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor", "sq_status_string")
 
 
 class SmoothQuantError(RuntimeError):
@@ -52,6 +53,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sq_norm_quant_fp8.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P]
     lib.smoothquant_fold_fp8.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
     lib.sq_fp8_gemm.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, P]
+    lib.sq_norm_quant_fp8_per_tensor.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P]
+    lib.sq_norm_quant_fp8_static.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P]
+    lib.sq_static_step_fp8.argtypes = [P, P, I64, P, P]
+    lib.smoothquant_fold_fp8_per_tensor.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
     lib.sq_status_string.argtypes = [I]
     lib.sq_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -129,6 +134,11 @@ def smoothquant_fold_per_tensor(act_absmax, w, alpha, eps=1e-5, norm="none", gam
     return _fold("smoothquant_fold_per_tensor", act_absmax, w, alpha, eps, norm, gamma, beta, out)
 
 
+def smoothquant_fold_fp8_per_tensor(act_absmax, w, alpha, eps=1e-5, norm="none", gamma=None, beta=None, out=None):
+    """As smoothquant_fold_fp8 with one weight step max |W-hat| / 448 for the whole tensor (codes saturated)."""
+    return _fold("smoothquant_fold_fp8_per_tensor", act_absmax, w, alpha, eps, norm, gamma, beta, out)
+
+
 def _fold(fn, act_absmax, w, alpha, eps, norm, gamma, beta, out):
     _dev(w, "w", _ACT)
     n, k = w.shape
@@ -143,7 +153,7 @@ def _fold(fn, act_absmax, w, alpha, eps, norm, gamma, beta, out):
         out.setdefault("beta_f", torch.empty(k, dtype=torch.float32, device=dev))
     else:
         out["beta_f"] = None
-    code_dt = torch.uint8 if fn.endswith("_fp8") else torch.int8
+    code_dt = torch.uint8 if "_fp8" in fn else torch.int8
     out.setdefault("wq", torch.empty(n, k, dtype=code_dt, device=dev))
     out.setdefault("w_scale", torch.empty(n, dtype=torch.float32, device=dev))
     for key, shp, dt in [("s", (k,), torch.float32), ("gamma_f", (k,), torch.float32),
@@ -178,8 +188,28 @@ def sq_norm_quant_static(x, step, norm="none", gamma_f=None, beta_f=None, eps=1e
     return _nq("sq_norm_quant_static", x, norm, gamma_f, beta_f, eps, xq, x_scale, step)
 
 
+def sq_norm_quant_fp8_per_tensor(x, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
+    """Fused norm + FP8 (E4M3) codes with one dynamic step max |y| / 448 for the whole tensor."""
+    return _nq("sq_norm_quant_fp8_per_tensor", x, norm, gamma_f, beta_f, eps, xq, x_scale)
+
+
+def sq_norm_quant_fp8_static(x, step, norm="none", gamma_f=None, beta_f=None, eps=1e-5, xq=None, x_scale=None):
+    """Fused norm + FP8 (E4M3) codes with a static step (a [1] fp32 device tensor), saturated to +-448."""
+    _dev(step, "step", torch.float32, (1,))
+    return _nq("sq_norm_quant_fp8_static", x, norm, gamma_f, beta_f, eps, xq, x_scale, step)
+
+
+def sq_static_step_fp8(act_absmax, s, step=None):
+    """Static FP8 activation step fl32(max_j fl32(a_j / s_j) / 448) into a [1] fp32 tensor."""
+    return _static_step("sq_static_step_fp8", act_absmax, s, step)
+
+
 def sq_static_step(act_absmax, s, step=None):
     """Static activation step fl32(max_j fl32(a_j / s_j) / 127) into a [1] fp32 tensor."""
+    return _static_step("sq_static_step", act_absmax, s, step)
+
+
+def _static_step(fn, act_absmax, s, step):
     k = act_absmax.shape[0]
     _dev(act_absmax, "act_absmax", torch.float32, (k,))
     _dev(s, "s", torch.float32, (k,))
@@ -187,7 +217,7 @@ def sq_static_step(act_absmax, s, step=None):
         step = torch.empty(1, dtype=torch.float32, device=s.device)
     _dev(step, "step", torch.float32, (1,))
     with torch.cuda.device(s.device):
-        _check("sq_static_step", lib.sq_static_step(_ptr(act_absmax), _ptr(s), k, _ptr(step), _stream(s)))
+        _check(fn, getattr(lib, fn)(_ptr(act_absmax), _ptr(s), k, _ptr(step), _stream(s)))
     return step
 
 
@@ -196,7 +226,7 @@ def _nq(fn, x, norm, gamma_f, beta_f, eps, xq, x_scale, *step):
     m, k = x.shape
     _dev(gamma_f, "gamma_f", torch.float32, (k,))
     _dev(beta_f, "beta_f", torch.float32, (k,))
-    code_dt = torch.uint8 if fn.endswith("_fp8") else torch.int8
+    code_dt = torch.uint8 if "_fp8" in fn else torch.int8
     if xq is None:
         xq = torch.empty(m, k, dtype=code_dt, device=x.device)
     if x_scale is None:

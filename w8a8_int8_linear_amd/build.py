@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsmoothquant.so")
 ARCH = os.environ.get("SQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["sq_validate.cpp", "sq_api.cpp", "k_rows.hip", "k_rows_tensor.hip", "k_rows_step.hip", "k_rows_fp8.hip", "k_gemm.hip"]
+SOURCES = ["sq_validate.cpp", "sq_api.cpp", "k_rows.hip", "k_rows_tensor.hip", "k_rows_step.hip", "k_rows_fp8.hip",
+           "k_rows_fp8_step.hip", "k_gemm.hip"]
 
 # Numerics: no contraction of separate roundings, IEEE fp32 divide/sqrt, binary32
 # denormals kept. Packed fp32 instructions are disabled for all device code.
@@ -59,7 +60,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every source and link the shared library; always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]

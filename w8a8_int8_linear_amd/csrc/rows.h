@@ -348,21 +348,23 @@ constexpr int kRowsPerRow = 0;       // one step per row (per-token activations,
 constexpr int kRowsAmax = 1;         // per-tensor first pass: each row's max |y| into x_scale[row]; no codes
 constexpr int kRowsGivenStep = 2;    // per-tensor codes with a step given for the whole tensor, clipped
 constexpr int kRowsFp8 = 3;          // one step per row, FP8 (OCP E4M3) codes: step = absmax / 448
+constexpr int kRowsFp8GivenStep = 4; // FP8 codes with a step given for the whole tensor, saturated to +-448
 
 // One row of a per-tensor pass: MODE kRowsAmax writes the row's max |y| alone
 // (the first pass of a per-tensor dynamic step); kRowsGivenStep writes the
 // codes of y with a step given for the whole tensor (the second pass, or a
-// static calibrated step), clipped to [-127, 127], and x_scale[row] = step if
-// write_scale. Either way NONE needs a single pass over the row: each vector's
+// static calibrated step), clipped to [-127, 127] (with the FP8 quantiser:
+// E4M3 codes saturated to +-448), and x_scale[row] = step if write_scale.
+// Either way NONE needs a single pass over the row: each vector's
 // raw buffer is refilled with the next row as soon as it has been read.
-template <int MODE, typename T, int NORM, int NV, int THREADS, int GREG, int GLDS>
+template <int MODE, typename T, int NORM, int NV, int THREADS, int GREG, int GLDS, typename Q>
 __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
                                                     int64_t row, int64_t next, int M, int K,
                                                     const float* __restrict__ gamma,
                                                     const ColVec<NV, THREADS, GREG, GLDS>& gv,
                                                     const float* __restrict__ beta, float eps,
                                                     int8_t* __restrict__ xq, float* __restrict__ x_scale,
-                                                    RedRing<THREADS>& red, int& rk, const Quantizer& qz,
+                                                    RedRing<THREADS>& red, int& rk, const Q& qz,
                                                     bool write_scale) {
   const int nvec = K >> 3;
   constexpr int B = Storage<T>::kBytes;
@@ -408,7 +410,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8<true>(ys[i]));
+        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.template codes8<true>(ys[i]));
       }
     } else {
 #pragma unroll
@@ -417,7 +419,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
         if (vi < nvec) {
           float y[8];
           none_y(raw, i, gv, y);
-          store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8<true>(y));
+          store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.template codes8<true>(y));
           if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
         }
       }
@@ -443,7 +445,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8<true>(v[i]));
+        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.template codes8<true>(v[i]));
       }
     }
   }
@@ -476,12 +478,15 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
   raw.load(x, blockIdx.x, K);
   gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
   int rk = 0;
-  if constexpr (MODE == kRowsAmax || MODE == kRowsGivenStep) {
-    // per-tensor passes (step_ptr and write_scale are used only here)
-    const Quantizer qz(MODE == kRowsGivenStep ? *step_ptr : 0.0f);
+  if constexpr (MODE == kRowsAmax || MODE == kRowsGivenStep || MODE == kRowsFp8GivenStep) {
+    // per-tensor passes (step_ptr and write_scale are used only here); the FP8
+    // code pass is the INT8 one with E4M3 codes
+    using Q = typename std::conditional<MODE == kRowsFp8GivenStep, QuantizerFp8, Quantizer>::type;
+    constexpr int kPass = MODE == kRowsFp8GivenStep ? kRowsGivenStep : MODE;
+    const Q qz(MODE == kRowsAmax ? 0.0f : *step_ptr);
     for (int64_t row = blockIdx.x; row < M; row += G)
-      quantize_row_tensor<MODE, T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale,
-                                                      red, rk, qz, write_scale != 0);
+      quantize_row_tensor<kPass, T, NORM, NV, THREADS>(raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale,
+                                                       red, rk, qz, write_scale != 0);
   } else {
     for (int64_t row = blockIdx.x; row < M; row += G)
       quantize_row<T, NORM, NV, THREADS, kReg, kLds, MODE == kRowsFp8>(raw, x, row, row + G, M, K, gamma, gv, beta,

@@ -77,7 +77,7 @@ sq_status sq_norm_quant_static(const void* x, sq_dtype x_dt, int64_t M, int64_t 
 
 sq_status sq_static_step(const float* act_absmax, const float* s, int64_t K, float* step, void* stream) {
   if (sq_status st = sq::check_static_step(act_absmax, s, K, step)) return st;
-  return from_hip(sq::launch_static_step(act_absmax, s, static_cast<int>(K), step, as_stream(stream)));
+  return from_hip(sq::launch_static_step(act_absmax, s, static_cast<int>(K), step, 127.0f, as_stream(stream)));
 }
 
 sq_status smoothquant_fold_per_tensor(const float* act_absmax, const void* w, sq_dtype w_dt, int64_t N, int64_t K,
@@ -127,6 +127,46 @@ sq_status sq_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq
   sq::GemmArgs g{xa, x_scale, wa, w_scale, bias, y, y_dt, static_cast<int>(M), static_cast<int>(N),
                  static_cast<int>(K)};
   return from_hip(sq::launch_gemm_fp8(g, as_stream(stream)));
+}
+
+sq_status sq_norm_quant_fp8_per_tensor(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm,
+                                       const float* gamma_f, const float* beta_f, float eps, uint8_t* xq,
+                                       float* x_scale, void* stream) {
+  int8_t* q = reinterpret_cast<int8_t*>(xq);
+  if (sq_status s = sq::check_norm_quant(x, x_dt, M, K, norm, gamma_f, beta_f, eps, q, x_scale)) return s;
+  sq::RowArgs a{x, x_dt, M, static_cast<int>(K), norm, gamma_f, beta_f, eps, q, x_scale, nullptr};
+  return from_hip(sq::launch_norm_quant_fp8_per_tensor(a, as_stream(stream)));
+}
+
+sq_status sq_norm_quant_fp8_static(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm,
+                                   const float* gamma_f, const float* beta_f, float eps, const float* step,
+                                   uint8_t* xq, float* x_scale, void* stream) {
+  int8_t* q = reinterpret_cast<int8_t*>(xq);
+  if (sq_status s = sq::check_norm_quant(x, x_dt, M, K, norm, gamma_f, beta_f, eps, q, x_scale)) return s;
+  if (!step) return SQ_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(step) % 4 != 0) return SQ_ERR_MISALIGNED;
+  sq::RowArgs a{x, x_dt, M, static_cast<int>(K), norm, gamma_f, beta_f, eps, q, x_scale, nullptr};
+  return from_hip(sq::launch_norm_quant_fp8_given_step(a, step, as_stream(stream)));
+}
+
+sq_status sq_static_step_fp8(const float* act_absmax, const float* s, int64_t K, float* step, void* stream) {
+  if (sq_status st = sq::check_static_step(act_absmax, s, K, step)) return st;
+  return from_hip(sq::launch_static_step(act_absmax, s, static_cast<int>(K), step, 448.0f, as_stream(stream)));
+}
+
+sq_status smoothquant_fold_fp8_per_tensor(const float* act_absmax, const void* w, sq_dtype w_dt, int64_t N,
+                                          int64_t K, double alpha, float eps, sq_norm norm, const float* gamma,
+                                          const float* beta, float* s_out, float* gamma_out, float* beta_out,
+                                          uint8_t* wq, float* w_scale, void* stream) {
+  int8_t* q = reinterpret_cast<int8_t*>(wq);
+  if (sq_status s = sq::check_fold(act_absmax, w, w_dt, N, K, alpha, eps, norm, gamma, beta, s_out, gamma_out,
+                                   beta_out, q, w_scale))
+    return s;
+  hipStream_t st = as_stream(stream);
+  sq::FoldArgs f{act_absmax, w, w_dt, N, K, alpha, eps, gamma, beta, s_out, gamma_out, beta_out};
+  if (sq_status s = from_hip(sq::launch_fold_colmax_scales(f, st))) return s;
+  sq::RowArgs r{w, w_dt, N, static_cast<int>(K), SQ_NORM_NONE, s_out, nullptr, 1.0f, q, w_scale, nullptr};
+  return from_hip(sq::launch_norm_quant_fp8_per_tensor(r, st));
 }
 
 const char* sq_status_string(sq_status s) {

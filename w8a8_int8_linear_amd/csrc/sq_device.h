@@ -309,8 +309,11 @@ __device__ __forceinline__ float fp8_step(float amax) { return div_rn(amax, 448.
 // normal or subnormal range alike) the codes come from exact quotients. The
 // step below saturates at +0 (a zero y keeps its zero code); below -0 it
 // wraps to a NaN pattern, which only sends those 8 values to the exact path.
-// |t| stays within 448 * (1 + 2^-23), below the 464 midpoint past which E4M3
-// has only NaN.
+// With the row's own step |t| stays within 448 * (1 + 2^-23), below the 464
+// midpoint past which E4M3 has only NaN. CLIP (a step given for a whole
+// tensor, which values may exceed) saturates both neighbours and the exact
+// quotients to [-448, 448] first; clamping is monotone, so the neighbour test
+// still decides.
 struct QuantizerFp8 {
   float step, rcp;
   bool zero, exact_only;
@@ -326,9 +329,9 @@ struct QuantizerFp8 {
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], w1, true);
     return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
   }
+  __device__ __forceinline__ static float sat(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
   template <bool CLIP = false>
   __device__ __forceinline__ uint2 codes8(const float y[8]) const {
-    static_assert(!CLIP, "FP8 codes use a step of their own row");
     if (zero) return make_uint2(0u, 0u);                 // workgroup-uniform
     float lo[8], hi[8];
 #pragma unroll
@@ -336,12 +339,16 @@ struct QuantizerFp8 {
       const uint32_t u = __float_as_uint(mul_rn(y[i], rcp));
       lo[i] = __uint_as_float(__builtin_elementwise_sub_sat(u, 4u));
       hi[i] = __uint_as_float(u + 4u);
+      if constexpr (CLIP) {
+        lo[i] = sat(lo[i]);
+        hi[i] = sat(hi[i]);
+      }
     }
     const uint2 a = pack8(lo), b = pack8(hi);
     if (!exact_only && a.x == b.x && a.y == b.y) return a;
     float t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = div_rn(y[i], step);
+    for (int i = 0; i < 8; ++i) t[i] = CLIP ? sat(div_rn(y[i], step)) : div_rn(y[i], step);
     return pack8(t);
   }
 };

@@ -65,7 +65,13 @@ hipError_t launch_norm_quant_per_tensor(const RowArgs& a, hipStream_t st);
 hipError_t launch_norm_quant_given_step(const RowArgs& a, const float* step, hipStream_t st);
 // As above; x_scale is written only if write_scale (it may then be the step's own buffer).
 hipError_t launch_rows_given_step(const RowArgs& a, const float* step, bool write_scale, hipStream_t st);
-// *step = fl32(max_j fl32(act_absmax[j] / s[j]) / 127).
-hipError_t launch_static_step(const float* act_absmax, const float* s, int K, float* step, hipStream_t st);
+// *step = fl32(max_j fl32(act_absmax[j] / s[j]) / qmax), qmax 127 (INT8) or 448 (FP8).
+hipError_t launch_static_step(const float* act_absmax, const float* s, int K, float* step, float qmax,
+                              hipStream_t st);
+// FP8 with one step for the whole tensor (E4M3 codes saturated to +-448): the
+// dynamic per-tensor passes with 448 for 127, and the code pass with a given step.
+hipError_t launch_norm_quant_fp8_per_tensor(const RowArgs& a, hipStream_t st);
+hipError_t launch_norm_quant_fp8_given_step(const RowArgs& a, const float* step, hipStream_t st);
+hipError_t launch_rows_given_step_fp8(const RowArgs& a, const float* step, bool write_scale, hipStream_t st);
 
 }  // namespace sq
