@@ -344,8 +344,9 @@ def median_ms(torch, fn, n):
 
 
 def granularity_sweep(args):
-    """Per-token vs per-tensor dynamic vs static activation steps (and per-channel vs per-tensor weight
-    steps in the fold) on the MT-NLG-width sites, HIP-event medians over 20 launches (fold: 5)."""
+    """Per-token vs per-tensor dynamic vs static activation steps, INT8 and FP8 (and per-channel vs
+    per-tensor weight steps in the fold) on the MT-NLG-width sites, HIP-event medians over 20 launches
+    (fold: 5)."""
     import torch
     import w8a8_int8_linear_amd as sq
     from synth import WORKLOADS
@@ -363,20 +364,32 @@ def granularity_sweep(args):
         g, b = fo["gamma_f"], fo["beta_f"]
         e = d["x"].element_size()
         nq_bytes = m * k * e + m * k + 4 * m + 4 * k * (2 if b is not None else 1)
+        stp8 = sq.sq_static_step_fp8(amax, fo["s"])
+        xq8 = torch.empty(m, k, dtype=torch.uint8, device="cuda")
         runs = [("per-token", lambda: sq.sq_norm_quant(d["x"], norm, g, b, EPS, d["xq"], d["xs"])),
                 ("per-tensor dynamic (2 passes)",
                  lambda: sq.sq_norm_quant_per_tensor(d["x"], norm, g, b, EPS, d["xq"], d["xs"])),
-                ("per-tensor static", lambda: sq.sq_norm_quant_static(d["x"], stp, norm, g, b, EPS, d["xq"], d["xs"]))]
+                ("per-tensor static", lambda: sq.sq_norm_quant_static(d["x"], stp, norm, g, b, EPS, d["xq"], d["xs"])),
+                ("FP8 per-token", lambda: sq.sq_norm_quant_fp8(d["x"], norm, g, b, EPS, xq8, d["xs"])),
+                ("FP8 per-tensor dynamic (2 passes)",
+                 lambda: sq.sq_norm_quant_fp8_per_tensor(d["x"], norm, g, b, EPS, xq8, d["xs"])),
+                ("FP8 per-tensor static",
+                 lambda: sq.sq_norm_quant_fp8_static(d["x"], stp8, norm, g, b, EPS, xq8, d["xs"]))]
         for name, fn in runs:
             ms = med(fn, 20)
             print(json.dumps({"stage": "norm_quant", "granularity": name, "site": d["site"].name, "shape": [m, k],
                               "ms": round(ms, 4), "GBps": round(nq_bytes / ms / 1e6, 1)}), flush=True)
         fold_bytes = 2 * n * k * e + n * k + 4 * n + 16 * k
+        f8 = {key: (torch.empty_like(v, dtype=torch.uint8) if key == "wq" else torch.empty_like(v))
+              for key, v in d["fold"].items()}
         for name, fn in [("per-channel", lambda: sq.smoothquant_fold(amax, d["w"], wl.alpha, EPS, norm, d["gamma"],
                                                                       d["beta"], out=d["fold"])),
                          ("per-tensor (3 weight passes)",
                           lambda: sq.smoothquant_fold_per_tensor(amax, d["w"], wl.alpha, EPS, norm, d["gamma"],
-                                                                 d["beta"], out=d["fold"]))]:
+                                                                 d["beta"], out=d["fold"])),
+                         ("FP8 per-tensor (3 weight passes)",
+                          lambda: sq.smoothquant_fold_fp8_per_tensor(amax, d["w"], wl.alpha, EPS, norm, d["gamma"],
+                                                                     d["beta"], out=f8))]:
             ms = med(fn, 5)
             print(json.dumps({"stage": "fold", "granularity": name, "site": d["site"].name, "shape": [n, k],
                               "ms": round(ms, 4), "GBps": round(fold_bytes / ms / 1e6, 1)}), flush=True)
@@ -408,10 +421,12 @@ def summarize_granularities(trace_dir):
         trace_dir, "activation and weight step granularities, MT-NLG-530B-width sites", GRAN_CMD,
         "--summarize-granularities",
         "Sites: LayerNorm 8192x20480 -> fc1 and NONE 8192x81920 -> fc2 (fp16), folds of their weights "
-        "(81920x20480, 20480x81920). The last template argument of `k_norm_quant` is its mode: 0 one step per "
-        "row, 1 the rows' maxima (first per-tensor pass), 2 codes with a step given for the whole tensor "
-        "(second per-tensor pass, or a static step); `k_tensor_step` reduces the rows' maxima to the tensor "
-        "step.", "kernel_stats_granularities_mtnlg530b.md")
+        "(81920x20480, 20480x81920). The last template argument of `k_norm_quant` is its mode: 0 one INT8 step "
+        "per row, 1 the rows' maxima (first per-tensor pass), 2 INT8 codes with a step given for the whole "
+        "tensor (second per-tensor pass, or a static step), 3 one FP8 step per row, 4 FP8 codes with a given "
+        "step (saturated to +-448); `k_tensor_step` reduces the rows' maxima to the tensor step (/127 or /448). "
+        "Each kernel's rows mix the activation passes and the fold's weight passes.",
+        "kernel_stats_granularities_mtnlg530b.md")
 
 
 # ----------------------------------------------------------------------------- FP8 (E4M3) against INT8
@@ -566,8 +581,13 @@ def accuracy_site(torch, sq, wl, si, m_tokens):
     def run(scheme, alpha, act, fold_fn, a_in):
         fo = fold_fn(a_in, w, 0.5 if alpha is None else alpha, EPS, norm, g, b)
         gf, bf = fo["gamma_f"], fo["beta_f"]
-        if act == "fp8":
-            xq, xs = sq.sq_norm_quant_fp8(x, norm, gf, bf, EPS)
+        if act.startswith("fp8"):
+            if act == "fp8":
+                xq, xs = sq.sq_norm_quant_fp8(x, norm, gf, bf, EPS)
+            elif act == "fp8 per-tensor":
+                xq, xs = sq.sq_norm_quant_fp8_per_tensor(x, norm, gf, bf, EPS)
+            else:
+                xq, xs = sq.sq_norm_quant_fp8_static(x, sq.sq_static_step_fp8(a_in, fo["s"]), norm, gf, bf, EPS)
             y = sq.sq_fp8_gemm(xq, xs, fo["wq"], fo["w_scale"], out_dtype=torch.float32)
             span = ordinary_span_fp8(xq, inp["outliers"])
         else:
@@ -593,6 +613,10 @@ def accuracy_site(torch, sq, wl, si, m_tokens):
         run("plain FP8 (E4M3), per-token X, per-channel W", None, "fp8", sq.smoothquant_fold_fp8, wmax)
         for alpha in ALPHAS:
             run("SmoothQuant FP8 (E4M3), per-token X, per-channel W", alpha, "fp8", sq.smoothquant_fold_fp8, amax)
+        run("SmoothQuant FP8 (E4M3) O2: per-tensor X and W", 0.5, "fp8 per-tensor",
+            sq.smoothquant_fold_fp8_per_tensor, amax)
+        run("SmoothQuant FP8 (E4M3) O3: static X, per-tensor W", 0.5, "fp8 static",
+            sq.smoothquant_fold_fp8_per_tensor, amax)
     return out
 
 

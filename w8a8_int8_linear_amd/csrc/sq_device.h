@@ -311,9 +311,10 @@ __device__ __forceinline__ float fp8_step(float amax) { return div_rn(amax, 448.
 // wraps to a NaN pattern, which only sends those 8 values to the exact path.
 // With the row's own step |t| stays within 448 * (1 + 2^-23), below the 464
 // midpoint past which E4M3 has only NaN. CLIP (a step given for a whole
-// tensor, which values may exceed) saturates both neighbours and the exact
-// quotients to [-448, 448] first; clamping is monotone, so the neighbour test
-// still decides.
+// tensor, which values may exceed) saturates t, and the exact quotients, to
+// [-448, 448] first: sat(q) then lies between the neighbours of sat(t) (both
+// sides of 448 are in one binade, and beyond 448 both neighbours take 448's
+// code), so the neighbour test still decides.
 struct QuantizerFp8 {
   float step, rcp;
   bool zero, exact_only;
@@ -336,13 +337,10 @@ struct QuantizerFp8 {
     float lo[8], hi[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t u = __float_as_uint(mul_rn(y[i], rcp));
+      const float t = mul_rn(y[i], rcp);
+      const uint32_t u = __float_as_uint(CLIP ? sat(t) : t);
       lo[i] = __uint_as_float(__builtin_elementwise_sub_sat(u, 4u));
       hi[i] = __uint_as_float(u + 4u);
-      if constexpr (CLIP) {
-        lo[i] = sat(lo[i]);
-        hi[i] = sat(hi[i]);
-      }
     }
     const uint2 a = pack8(lo), b = pack8(hi);
     if (!exact_only && a.x == b.x && a.y == b.y) return a;
