@@ -1,0 +1,96 @@
+"""Host logic of bench.py on the CPU: the refusal of runs on several GPUs, the counter summaries it
+derives from rocprofv3 CSVs (shader clock and MFMA busy, per-dispatch kernel tables), the traffic
+record's staleness check, and the algorithmic byte counts. Synthetic CSVs stand in for rocprofv3
+output; nothing here touches a GPU or the committed profiles."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture
+def scratch_root(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "profiles" / "traffic.json"))
+    return tmp_path
+
+
+def _write_csv(path, header, rows):
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_ALL)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_runs_on_several_gpus_are_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "error" in out and out["n_gpus"] == 2
+
+
+def test_gemm_clock_from_counters(tmp_path):
+    header = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    # dispatch 5: 18e6 cycles per XCD in 10 ms -> 1.8 GHz; MFMA busy 70% of every SIMD's cycles
+    for name, val in [("GRBM_GUI_ACTIVE", 8 * 18e6), ("SQ_VALU_MFMA_BUSY_CYCLES", 256 * 4 * 18e6 * 0.7),
+                      ("SQ_BUSY_CYCLES", 1.0)]:
+        rows.append([5, "void sq::k_gemm_tile<1>(...)", name, val, 1_000_000, 11_000_000])
+    rows.append([6, "void sq::k_norm_quant<...>(...)", "GRBM_GUI_ACTIVE", 1.0, 0, 10])
+    _write_csv(tmp_path / "clk" / "run_counter_collection.csv", header, rows)
+    clk = bench.gemm_clock(str(tmp_path / "clk"))
+    assert len(clk) == 1
+    assert clk[0]["ms"] == pytest.approx(10.0)
+    assert clk[0]["sclk_GHz"] == pytest.approx(1.8)
+    assert clk[0]["mfma_busy"] == pytest.approx(0.7)
+
+
+def test_fp8_table_splits_a_kernel_serving_two_row_counts(scratch_root):
+    header = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    rows, t = [], 0
+    for ms in [0.35] * 7 + [0.88] * 7:                                   # activations, then fold weights
+        rows.append(["void sq::k_norm_quant<sq::f16_t, 0, 20, 512, 0>(...)", 131072, 512, t, t + int(ms * 1e6)])
+        t += 2_000_000
+    for ms in [0.0047] + [0.0021] * 13:                                  # one slow first launch: not split
+        rows.append(["void sq::k_fill_zero(...)", 81920, 256, t, t + int(ms * 1e6)])
+        t += 10_000
+    rows.append(["void at::native::other(...)", 1, 1, 0, 5])
+    _write_csv(scratch_root / "tr" / "run_kernel_trace.csv", header, rows)
+    bench.summarize_fp8(str(scratch_root / "tr"))
+    text = (scratch_root / "profiles" / "kernel_trace_fp8_mtnlg530b.md").read_text()
+    nq = [ln for ln in text.splitlines() if ln.startswith("| `sq::k_norm_quant")]
+    assert len(nq) == 2 and all("| 7 |" in ln for ln in nq)
+    assert "0.8800" in nq[0] and "0.3500" in nq[1]                       # slower group first
+    fz = [ln for ln in text.splitlines() if ln.startswith("| `sq::k_fill_zero")]
+    assert len(fz) == 1 and "| 14 |" in fz[0]
+    assert "at::native" not in text
+
+
+def test_traffic_record_goes_stale_with_the_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "traffic.json"))
+    rec = {"source_sha256": bench.gemm_source_hash(), "traffic_bytes_per_launch": 1.0}
+    with open(bench.TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f)
+    assert bench.recorded_traffic()["traffic_bytes_per_launch"] == 1.0
+    rec["source_sha256"] = "0" * 64
+    with open(bench.TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f)
+    assert bench.recorded_traffic() is None
+    os.remove(bench.TRAFFIC_JSON)
+    assert bench.recorded_traffic() is None
+
+
+def test_decode_bytes_counts_weights_tokens_scales_and_output():
+    # N*K weight codes + M*K token codes + 4 (M + N) scale bytes + 2 M N fp16 outputs
+    assert bench.decode_bytes(1, 9216) == 9216 * 9216 + 9216 + 4 * (1 + 9216) + 2 * 9216
+    assert bench.decode_bytes(64, 36864, 9216) == 36864 * 9216 + 64 * 9216 + 4 * (64 + 36864) + 2 * 64 * 36864
