@@ -230,7 +230,9 @@ GEMM_SHAPES = [(17, 33, 128), (256, 256, 128), (300, 520, 384), (513, 700, 1280)
                (1024, 2048, 20480), (5, 9, 133120),
                # decode (M <= 64): every token-tile count, narrow and 144-channel strips, ragged N
                (1, 9216, 9216), (2, 1000, 1280), (4, 36864, 9216), (16, 130, 384), (33, 4000, 2048),
-               (48, 16400, 1024), (64, 36864, 9216), (65, 300, 256)]
+               (48, 16400, 1024), (64, 36864, 9216), (65, 300, 256),
+               # N not a multiple of 4: the epilogue's partial stores, prefill and decode
+               (130, 45, 256), (300, 1001, 384), (40, 37, 640)]
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
