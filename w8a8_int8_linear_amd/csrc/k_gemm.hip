@@ -654,9 +654,11 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 //
 // FP8 (E4M3 codes, K % 128 == 0): one v_mfma_scale_f32_16x16x128_f8f6f4 takes a
 // whole segment (K bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of a row for
-// lane group g, as in the prefill kernel), so the wave pairs split the
-// segments by parity instead of the K steps, into binary32 accumulators, and
-// the two partials meet through LDS the same way.
+// lane group g, as in the prefill kernel), so a segment cannot be split by K
+// step. Every wave instead works on every segment, on its own block of
+// channel tiles x token tiles (a 2 x 2 grid of channel and token halves with
+// two or more token tiles, else channel quarters), into binary32
+// accumulators; each wave then stores its own outputs, with no reduction.
 constexpr int kDecNowhere = 0x40000000;               // a buffer offset past every operand: loads return zeros
 constexpr int kDec2Seg = 128;
 constexpr int kDec2Tile = 16 * kDec2Seg;             // LDS bytes of one 16-row operand tile
@@ -677,6 +679,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
   constexpr int kStage = kTiles * kDec2Tile + (kSink ? 1024 : 0);
   constexpr int NH = (NT + 1) / 2;                               // channel tiles per half (the second may have one fewer)
   static_assert(kStage >= NH * MT * 1024, "a stage holds one wave's partial accumulators");
+  // FP8 wave grid: WU token groups x (kDecWaves / WU) channel groups, NC x MU tiles per wave
+  constexpr int WU = FP8 && MT >= 2 ? 2 : 1;
+  constexpr int NC = (NT + kDecWaves / WU - 1) / (kDecWaves / WU);
+  constexpr int MU = (MT + WU - 1) / WU;
   __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
   __shared__ __attribute__((aligned(1024))) int8_t st1[kStage];
   __shared__ __attribute__((aligned(1024))) int8_t st2[kStage];
@@ -740,11 +746,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
   const int frag = r16 * kDec2Seg + 16 * (c ^ swz2(r16));
   const int frag_lo = r16 * kDec2Seg + 16 * ((lane >> 4) ^ swz2(r16));          // FP8: both chunks of lane group g
   const int frag_hi = r16 * kDec2Seg + 16 * ((4 + (lane >> 4)) ^ swz2(r16));
-  AccV acc[NH][MT];
+  constexpr int AJ = FP8 ? NC : NH, AU = FP8 ? MU : MT;         // accumulator tiles of this wave
+  const int c0 = (wid / WU) * NC, u0 = (wid % WU) * MU;         // FP8: first channel / token tile of this wave
+  AccV acc[AJ][AU];
 #pragma unroll
-  for (int j = 0; j < NH; ++j)
+  for (int j = 0; j < AJ; ++j)
 #pragma unroll
-    for (int u = 0; u < MT; ++u) acc[j][u] = AccV{0, 0, 0, 0};
+    for (int u = 0; u < AU; ++u) acc[j][u] = AccV{0, 0, 0, 0};
 
 #define SQ_DEC_PRO(I) \
   if constexpr (I < R - 1) { issue(std::integral_constant<int, I>{}, I); memory_opaque(); }
@@ -757,29 +765,29 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
     stage_barrier();
     issue(std::integral_constant<int, (kk + R - 1) % R>{}, seg + R - 1);
     if constexpr (FP8) {
-      if ((seg & 1) == t) {
+      if (c0 < NT && u0 < MT) {                                  // uniform: a wave past the tiles only waits
         const uint32_t b = lds_addr(stage(k));
-        uint32_t addr[2 * (NH + MT)];
+        uint32_t addr[2 * (NC + MU)];
 #pragma unroll
-        for (int j = 0; j < NH; ++j) {
-          const uint32_t tb = b + min(h * NH + j, NT - 1) * kDec2Tile;
+        for (int j = 0; j < NC; ++j) {
+          const uint32_t tb = b + min(c0 + j, NT - 1) * kDec2Tile;
           addr[2 * j] = tb + frag_lo;
           addr[2 * j + 1] = tb + frag_hi;
         }
 #pragma unroll
-        for (int u = 0; u < MT; ++u) {
-          const uint32_t tb = b + (NT + u) * kDec2Tile;
-          addr[2 * (NH + u)] = tb + frag_lo;
-          addr[2 * (NH + u) + 1] = tb + frag_hi;
+        for (int u = 0; u < MU; ++u) {
+          const uint32_t tb = b + (NT + min(u0 + u, MT - 1)) * kDec2Tile;
+          addr[2 * (NC + u)] = tb + frag_lo;
+          addr[2 * (NC + u) + 1] = tb + frag_hi;
         }
-        v4i f[2 * (NH + MT)];
+        v4i f[2 * (NC + MU)];
         lds_read_frags(f, addr);
 #pragma unroll
-        for (int j = 0; j < NH; ++j) {
+        for (int j = 0; j < NC; ++j) {
           const v8i fw = __builtin_shufflevector(f[2 * j], f[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int u = 0; u < MT; ++u) {
-            const v8i fx = __builtin_shufflevector(f[2 * (NH + u)], f[2 * (NH + u) + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+          for (int u = 0; u < MU; ++u) {
+            const v8i fx = __builtin_shufflevector(f[2 * (NC + u)], f[2 * (NC + u) + 1], 0, 1, 2, 3, 4, 5, 6, 7);
             acc[j][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw, fx, acc[j][u], 0, 0, 0, 127, 0, 127);
           }
         }
@@ -812,8 +820,23 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
   SQ_DEC_TAIL(0) SQ_DEC_TAIL(1) SQ_DEC_TAIL(2) SQ_DEC_TAIL(3) SQ_DEC_TAIL(4) SQ_DEC_TAIL(5) SQ_DEC_TAIL(6)
 #undef SQ_DEC_TAIL
 
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                    // no DMA into LDS outlives the loop
+  if constexpr (FP8) {
+    // every wave stores its own channel x token tiles
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (c0 + j >= NT) continue;                                  // uniform
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        if (u0 + u >= MT) continue;                                // uniform
+        const int m = 16 * (u0 + u) + (lane & 15);
+        const int n = n0 + 16 * (c0 + j) + 4 * (lane >> 4);
+        if (m < M && n < N) store4<YDT>(y, N, m, n, acc[j][u], xs[m], ws, bias);
+      }
+    }
+    return;
+  }
   // K step 1's partials (waves 1, 3) join K step 0's (waves 0, 2) through LDS
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   stage_barrier();
   int8_t* park = h == 0 ? st0 : st1;
   if (t == 1) {
