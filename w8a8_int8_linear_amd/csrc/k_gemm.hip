@@ -648,17 +648,17 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 // r * 128, chunk c at slot c ^ swz2(r)), and DMA blocks of 8 rows x 128 bytes,
 // two per tile. A workgroup owns NT channel tiles (up to 9: a 144-channel
 // strip, so 36864 channels make exactly 256 workgroups and each xq segment
-// serves NT weight tiles). The four waves split each segment as (K step
-// = wave & 1, channel-tile half = wave >> 1); the two K steps' partials are
-// summed through LDS at the end. Segments go through an R-stage ring.
+// serves NT weight tiles). Every wave works on every segment, on its own
+// block of channel tiles x token tiles (a 2 x 2 grid of channel and token
+// halves with two or more token tiles, else channel quarters), and stores its
+// own outputs: no partial sums pass between waves. Segments go through an
+// R-stage ring.
 //
-// FP8 (E4M3 codes, K % 128 == 0): one v_mfma_scale_f32_16x16x128_f8f6f4 takes a
-// whole segment (K bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of a row for
-// lane group g, as in the prefill kernel), so a segment cannot be split by K
-// step. Every wave instead works on every segment, on its own block of
-// channel tiles x token tiles (a 2 x 2 grid of channel and token halves with
-// two or more token tiles, else channel quarters), into binary32
-// accumulators; each wave then stores its own outputs, with no reduction.
+// INT8: two v_mfma_i32_16x16x64_i8 per tile and segment, one per 64-byte half
+// (the second skipped on an odd last K step, whose bytes belong to the next
+// row). FP8 (E4M3 codes, K % 128 == 0): one v_mfma_scale_f32_16x16x128_f8f6f4
+// takes the whole segment (K bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of a
+// row for lane group g, as in the prefill kernel), into binary32 accumulators.
 constexpr int kDecNowhere = 0x40000000;               // a buffer offset past every operand: loads return zeros
 constexpr int kDec2Seg = 128;
 constexpr int kDec2Tile = 16 * kDec2Seg;             // LDS bytes of one 16-row operand tile
@@ -677,10 +677,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
   constexpr int kPerWave = kWPer + kXPer;                          // DMA instructions per wave per segment
   constexpr bool kSink = (2 * NT) % kDecWaves != 0 || (2 * MT) % kDecWaves != 0;   // padding DMAs need a sink
   constexpr int kStage = kTiles * kDec2Tile + (kSink ? 1024 : 0);
-  constexpr int NH = (NT + 1) / 2;                               // channel tiles per half (the second may have one fewer)
-  static_assert(kStage >= NH * MT * 1024, "a stage holds one wave's partial accumulators");
-  // FP8 wave grid: WU token groups x (kDecWaves / WU) channel groups, NC x MU tiles per wave
-  constexpr int WU = FP8 && MT >= 2 ? 2 : 1;
+  // wave grid: WU token groups x (kDecWaves / WU) channel groups, NC x MU tiles per wave
+  constexpr int WU = MT >= 2 ? 2 : 1;
   constexpr int NC = (NT + kDecWaves / WU - 1) / (kDecWaves / WU);
   constexpr int MU = (MT + WU - 1) / WU;
   __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
@@ -738,21 +736,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
     }
   };
 
-  // compute share: K step t of each segment (FP8: the segments of parity t),
-  // channel tiles [h NH, h NH + NH) (clipped to NT)
+  // compute share: channel tiles [c0, c0 + NC) x token tiles [u0, u0 + MU) of
+  // every segment (clipped to NT, MT); lane group g reads its 16 bytes of
+  // each 64-byte half of the segment's rows
   using AccV = std::conditional_t<FP8, v4f, v4i>;
-  const int t = wid & 1, h = wid >> 1;
-  const int c = 4 * t + (lane >> 4), r16 = lane & 15;
-  const int frag = r16 * kDec2Seg + 16 * (c ^ swz2(r16));
-  const int frag_lo = r16 * kDec2Seg + 16 * ((lane >> 4) ^ swz2(r16));          // FP8: both chunks of lane group g
+  const int r16 = lane & 15;
+  const int frag_lo = r16 * kDec2Seg + 16 * ((lane >> 4) ^ swz2(r16));
   const int frag_hi = r16 * kDec2Seg + 16 * ((4 + (lane >> 4)) ^ swz2(r16));
-  constexpr int AJ = FP8 ? NC : NH, AU = FP8 ? MU : MT;         // accumulator tiles of this wave
-  const int c0 = (wid / WU) * NC, u0 = (wid % WU) * MU;         // FP8: first channel / token tile of this wave
-  AccV acc[AJ][AU];
+  const int c0 = (wid / WU) * NC, u0 = (wid % WU) * MU;
+  AccV acc[NC][MU];
 #pragma unroll
-  for (int j = 0; j < AJ; ++j)
+  for (int j = 0; j < NC; ++j)
 #pragma unroll
-    for (int u = 0; u < AU; ++u) acc[j][u] = AccV{0, 0, 0, 0};
+    for (int u = 0; u < MU; ++u) acc[j][u] = AccV{0, 0, 0, 0};
 
 #define SQ_DEC_PRO(I) \
   if constexpr (I < R - 1) { issue(std::integral_constant<int, I>{}, I); memory_opaque(); }
@@ -764,24 +760,24 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 2) * kPerWave));
     stage_barrier();
     issue(std::integral_constant<int, (kk + R - 1) % R>{}, seg + R - 1);
-    if constexpr (FP8) {
-      if (c0 < NT && u0 < MT) {                                  // uniform: a wave past the tiles only waits
-        const uint32_t b = lds_addr(stage(k));
-        uint32_t addr[2 * (NC + MU)];
+    if (c0 < NT && u0 < MT) {                                    // uniform: a wave past the tiles only waits
+      const uint32_t b = lds_addr(stage(k));
+      uint32_t addr[2 * (NC + MU)];
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
-          const uint32_t tb = b + min(c0 + j, NT - 1) * kDec2Tile;
-          addr[2 * j] = tb + frag_lo;
-          addr[2 * j + 1] = tb + frag_hi;
-        }
+      for (int j = 0; j < NC; ++j) {
+        const uint32_t tb = b + min(c0 + j, NT - 1) * kDec2Tile;
+        addr[2 * j] = tb + frag_lo;
+        addr[2 * j + 1] = tb + frag_hi;
+      }
 #pragma unroll
-        for (int u = 0; u < MU; ++u) {
-          const uint32_t tb = b + (NT + min(u0 + u, MT - 1)) * kDec2Tile;
-          addr[2 * (NC + u)] = tb + frag_lo;
-          addr[2 * (NC + u) + 1] = tb + frag_hi;
-        }
-        v4i f[2 * (NC + MU)];
-        lds_read_frags(f, addr);
+      for (int u = 0; u < MU; ++u) {
+        const uint32_t tb = b + (NT + min(u0 + u, MT - 1)) * kDec2Tile;
+        addr[2 * (NC + u)] = tb + frag_lo;
+        addr[2 * (NC + u) + 1] = tb + frag_hi;
+      }
+      v4i f[2 * (NC + MU)];
+      lds_read_frags(f, addr);
+      if constexpr (FP8) {
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
           const v8i fw = __builtin_shufflevector(f[2 * j], f[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -791,20 +787,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
             acc[j][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw, fx, acc[j][u], 0, 0, 0, 127, 0, 127);
           }
         }
+      } else {
+        const bool two = 2 * seg + 1 < steps;                    // uniform: an odd last K step has one half
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+#pragma unroll
+          for (int u = 0; u < MU; ++u) {
+            acc[j][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[2 * j], f[2 * (NC + u)], acc[j][u], 0, 0, 0);
+            if (two)
+              acc[j][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[2 * j + 1], f[2 * (NC + u) + 1], acc[j][u], 0, 0, 0);
+          }
       }
-    } else if (2 * seg + t < steps) {
-      const uint32_t base = lds_addr(stage(k)) + frag;
-      uint32_t addr[NH + MT];
-#pragma unroll
-      for (int j = 0; j < NH; ++j) addr[j] = base + min(h * NH + j, NT - 1) * kDec2Tile;
-#pragma unroll
-      for (int u = 0; u < MT; ++u) addr[NH + u] = base + (NT + u) * kDec2Tile;
-      v4i f[NH + MT];
-      lds_read_frags(f, addr);
-#pragma unroll
-      for (int j = 0; j < NH; ++j)
-#pragma unroll
-        for (int u = 0; u < MT; ++u) acc[j][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[j], f[NH + u], acc[j][u], 0, 0, 0);
     }
   };
   int base = 0;
@@ -821,42 +814,16 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
 #undef SQ_DEC_TAIL
 
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                    // no DMA into LDS outlives the loop
-  if constexpr (FP8) {
-    // every wave stores its own channel x token tiles
+  // every wave stores its own channel x token tiles
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (c0 + j >= NT) continue;                                  // uniform
+  for (int j = 0; j < NC; ++j) {
+    if (c0 + j >= NT) continue;                                    // uniform
 #pragma unroll
-      for (int u = 0; u < MU; ++u) {
-        if (u0 + u >= MT) continue;                                // uniform
-        const int m = 16 * (u0 + u) + (lane & 15);
-        const int n = n0 + 16 * (c0 + j) + 4 * (lane >> 4);
-        if (m < M && n < N) store4<YDT>(y, N, m, n, acc[j][u], xs[m], ws, bias);
-      }
-    }
-    return;
-  }
-  // K step 1's partials (waves 1, 3) join K step 0's (waves 0, 2) through LDS
-  stage_barrier();
-  int8_t* park = h == 0 ? st0 : st1;
-  if (t == 1) {
-#pragma unroll
-    for (int j = 0; j < NH; ++j)
-#pragma unroll
-      for (int u = 0; u < MT; ++u) reinterpret_cast<AccV*>(park)[(j * MT + u) * 64 + lane] = acc[j][u];
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  stage_barrier();
-  if (t == 1) return;
-#pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    if (h * NH + j >= NT) continue;                              // uniform
-#pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      const AccV v = acc[j][u] + reinterpret_cast<const AccV*>(park)[(j * MT + u) * 64 + lane];
-      const int m = 16 * u + (lane & 15);
-      const int n = n0 + 16 * (h * NH + j) + 4 * (lane >> 4);
-      if (m < M && n < N) store4<YDT>(y, N, m, n, v, (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
+    for (int u = 0; u < MU; ++u) {
+      if (u0 + u >= MT) continue;                                  // uniform
+      const int m = 16 * (u0 + u) + (lane & 15);
+      const int n = n0 + 16 * (c0 + j) + 4 * (lane >> 4);
+      if (m < M && n < N) store4<YDT>(y, N, m, n, acc[j][u], (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
     }
   }
 }
