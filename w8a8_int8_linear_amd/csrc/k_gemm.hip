@@ -649,16 +649,31 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 // two per tile. A workgroup owns NT channel tiles (up to 9: a 144-channel
 // strip, so 36864 channels make exactly 256 workgroups and each xq segment
 // serves NT weight tiles). Every wave works on every segment, on its own
-// block of channel tiles x token tiles (a 2 x 2 grid of channel and token
-// halves with two or more token tiles, else channel quarters), and stores its
-// own outputs: no partial sums pass between waves. Segments go through an
-// R-stage ring.
+// block of channel tiles x token tiles (1, 2 or 4 token groups times 4, 2 or
+// 1 channel groups, whichever leaves the busiest wave the fewest tiles), and
+// stores its own outputs: no partial sums pass between waves. Segments go
+// through an R-stage ring.
 //
 // INT8: two v_mfma_i32_16x16x64_i8 per tile and segment, one per 64-byte half
 // (the second skipped on an odd last K step, whose bytes belong to the next
 // row). FP8 (E4M3 codes, K % 128 == 0): one v_mfma_scale_f32_16x16x128_f8f6f4
 // takes the whole segment (K bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of a
 // row for lane group g, as in the prefill kernel), into binary32 accumulators.
+// Token groups of the decode wave grid (1, 2 or 4; the channel groups take the
+// rest of the four waves): the fewest tiles on the busiest wave, then the
+// fewest fragment reads per segment.
+constexpr int dec_token_groups(int nt, int mt) {
+  int best = 1, best_tiles = 1 << 30, best_reads = 1 << 30;
+  for (int wu = 1; wu <= kDecWaves; wu *= 2) {
+    const int nc = (nt + kDecWaves / wu - 1) / (kDecWaves / wu), mu = (mt + wu - 1) / wu;
+    if (nc * mu < best_tiles || (nc * mu == best_tiles && nc + mu < best_reads)) {
+      best = wu;
+      best_tiles = nc * mu;
+      best_reads = nc + mu;
+    }
+  }
+  return best;
+}
 constexpr int kDecNowhere = 0x40000000;               // a buffer offset past every operand: loads return zeros
 constexpr int kDec2Seg = 128;
 constexpr int kDec2Tile = 16 * kDec2Seg;             // LDS bytes of one 16-row operand tile
@@ -678,7 +693,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
   constexpr bool kSink = (2 * NT) % kDecWaves != 0 || (2 * MT) % kDecWaves != 0;   // padding DMAs need a sink
   constexpr int kStage = kTiles * kDec2Tile + (kSink ? 1024 : 0);
   // wave grid: WU token groups x (kDecWaves / WU) channel groups, NC x MU tiles per wave
-  constexpr int WU = MT >= 2 ? 2 : 1;
+  constexpr int WU = dec_token_groups(NT, MT);
   constexpr int NC = (NT + kDecWaves / WU - 1) / (kDecWaves / WU);
   constexpr int MU = (MT + WU - 1) / WU;
   __shared__ __attribute__((aligned(1024))) int8_t st0[kStage];
