@@ -252,6 +252,24 @@ def test_fp8_gemm_accumulator(shape):
     assert np.all(err <= tol), f"max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3g}"
 
 
+# Every token count the FP8 decode kernel serves (1..64) and so every wave grid it picks, on a ragged
+# narrow strip and on the 144-channel strips, three 128-byte segments.
+@pytest.mark.parametrize("m", list(range(1, 65)))
+@pytest.mark.parametrize("n", [300, 16400])
+def test_fp8_gemm_decode_every_token_count(m, n):
+    k = 384
+    xq = _codes((m, k), 500 + m, 40.0)
+    wq = _codes((n, k), 600 + n, 0.5)
+    ones_m, ones_n = torch.ones(m, device="cuda"), torch.ones(n, device="cuda")
+    y = sq.sq_fp8_gemm(torch.from_numpy(xq).cuda(), ones_m, torch.from_numpy(wq).cuda(), ones_n,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    mi, ni = _positions(m, n, k, m * n)
+    exact, tol = fp8_gemm_tolerance(xq, wq, mi, ni)
+    err = np.abs(host(y)[mi, ni].astype(np.float64) - exact)
+    assert np.all(err <= tol), f"max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3g}"
+
+
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_fp8_gemm_dequantised_output(out):
     m, n, k = 300, 520, 1280

@@ -196,6 +196,23 @@ def test_gemm_i32_exact(mnk):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
 
 
+
+# The decode kernel picks its wave grid (token groups x channel groups) from the token-tile count and
+# the strip width: every token count it serves, on a ragged narrow strip and on the 144-channel strips,
+# with an odd number of 64-byte K steps (the last segment's second half is the next row's bytes).
+@pytest.mark.parametrize("m", list(range(5, 65)))
+@pytest.mark.parametrize("nk", [(300, 192), (16400, 320)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_decode_every_token_count(m, nk):
+    n, k = nk
+    xq = rand_int8((m, k), 300 + m)
+    wq = rand_int8((n, k), 400 + n)
+    acc = sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    ref = O.int_gemm(xq.numpy(), wq.numpy())
+    got = host(acc).astype(np.int64)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
+
+
 def test_gemm_int32_range_at_max_k():
     k = sq.SQ_K_MAX
     for m in [3, 70]:                                        # GEMV and tiled kernels
