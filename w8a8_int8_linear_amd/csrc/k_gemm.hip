@@ -650,8 +650,8 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 // strip, so 36864 channels make exactly 256 workgroups and each xq segment
 // serves NT weight tiles). Every wave works on every segment, on its own
 // block of channel tiles x token tiles (1, 2 or 4 token groups times 4, 2 or
-// 1 channel groups, whichever leaves the busiest wave the fewest tiles), and
-// stores its own outputs: no partial sums pass between waves. Segments go
+// 1 channel groups, whichever leaves the busiest wave the least MFMA and LDS
+// work), and stores its own outputs: no partial sums pass between waves. Segments go
 // through an R-stage ring.
 //
 // INT8: two v_mfma_i32_16x16x64_i8 per tile and segment, one per 64-byte half
@@ -660,16 +660,19 @@ __device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[
 // takes the whole segment (K bytes 16g .. 16g+15 and 64+16g .. 64+16g+15 of a
 // row for lane group g, as in the prefill kernel), into binary32 accumulators.
 // Token groups of the decode wave grid (1, 2 or 4; the channel groups take the
-// rest of the four waves): the fewest tiles on the busiest wave, then the
-// fewest fragment reads per segment.
+// rest of the four waves). The busiest wave's cost per segment is weighed as
+// 2 x its tiles (two INT8 MFMAs or one FP8 MFMA each) + its fragment-tile
+// reads from LDS (one per channel tile and per token tile), and the lowest
+// cost wins, the fewest token groups on a tie. Measured at K = 9216: with three
+// channel and three token tiles one token group beat a 2 x 2 grid by 13%; with
+// nine channel and four token tiles the 2 x 2 grid beat four token groups by 1%.
 constexpr int dec_token_groups(int nt, int mt) {
-  int best = 1, best_tiles = 1 << 30, best_reads = 1 << 30;
+  int best = 1, best_cost = 1 << 30;
   for (int wu = 1; wu <= kDecWaves; wu *= 2) {
     const int nc = (nt + kDecWaves / wu - 1) / (kDecWaves / wu), mu = (mt + wu - 1) / wu;
-    if (nc * mu < best_tiles || (nc * mu == best_tiles && nc + mu < best_reads)) {
+    if (2 * nc * mu + nc + mu < best_cost) {
       best = wu;
-      best_tiles = nc * mu;
-      best_reads = nc + mu;
+      best_cost = 2 * nc * mu + nc + mu;
     }
   }
   return best;
