@@ -89,3 +89,20 @@ def test_norm_quant_fp8_per_tensor_is_the_norm_then_the_tensor_quantiser():
         q, xs, info = O.norm_quant_fp8_per_tensor(x, "f32", "layernorm", g, b, 1e-5, step)
         q2, s2 = O.quantize_tensor_fp8(info["y"], step)
         assert np.array_equal(q, q2) and np.all(xs == s2)
+
+
+def test_the_tensor_max_sets_every_row_step():
+    # doubling the row that holds the tensor max doubles the one step, so every other row's codes
+    # shrink; with a step per row they would not move
+    rng = np.random.default_rng(8)
+    y = (rng.standard_normal((6, 48)) * 20).astype(F32)
+    y[2, 5] = 150.0
+    q1, s1 = O.quantize_tensor_fp8(y)
+    y2 = y.copy()
+    y2[2] *= F32(2)
+    q2, s2 = O.quantize_tensor_fp8(y2)
+    assert s2 == F32(2) * s1
+    d1, d2 = np.abs(O.e4m3_decode(q1)), np.abs(O.e4m3_decode(q2))
+    others = np.arange(6) != 2
+    assert np.all(d2[others].max(axis=1) < d1[others].max(axis=1))
+    assert d1[2].max() == d2[2].max() == 448.0
