@@ -85,6 +85,57 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n
   }
 }
 
+// store4 with the weight scales of the four outputs already in registers (w
+// holds ws[n .. n+3], clamped to the last column): the same roundings, for an
+// epilogue that must not wait on memory issued after the scales. The bias, when
+// there is one, is read here.
+template <int YDT>
+__device__ __forceinline__ void store4_pre(void* __restrict__ y, int N, int m, int n, const v4i acc, float xs,
+                                           const float (&w)[4], const float* __restrict__ bias) {
+  const int64_t off = static_cast<int64_t>(m) * N + n;
+  const bool full = (n + 3 < N) && ((N & 3) == 0);
+  if constexpr (YDT == SQ_DT_I32) {
+    int* p = static_cast<int*>(y) + off;
+    if (full) {
+      *reinterpret_cast<int4*>(p) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) p[r] = acc[r];
+    }
+  } else {
+    float o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = mul_rn(mul_rn(static_cast<float>(acc[r]), xs), w[r]);
+      if (bias) t = add_rn(t, bias[min(n + r, N - 1)]);
+      o[r] = t;
+    }
+    if constexpr (YDT == SQ_DT_F32) {
+      float* p = static_cast<float*>(y) + off;
+      if (full) {
+        *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) p[r] = o[r];
+      }
+    } else {
+      uint32_t h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = (YDT == SQ_DT_F16) ? f32_to_f16_rne(o[r]) : f32_to_bf16_rne(o[r]);
+      uint16_t* p = static_cast<uint16_t*>(y) + off;
+      if (full) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) p[r] = static_cast<uint16_t>(h[r]);
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- tiled kernel
 
 constexpr int kTile = 256;                     // output tile edge (m and n)
@@ -298,6 +349,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_k64(const int8_t* __restri
   }
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const int8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+
+// Fragment reads written in asm: at the top of the ring loop the compiler no
+// longer knows which stage each outstanding DMA writes and would drain them
+// all (vmcnt(0)) before a plain LDS read. The DMA data is already covered by
+// the explicit vmcnt wait ahead of the stage barrier; each asm statement waits
+// for its own reads before its outputs are used.
+template <int N>
+__device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[N]) {
+  int i = 0;
+#pragma unroll
+  for (; i + 4 <= N; i += 4)
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[i]), "=&v"(r[i + 1]), "=&v"(r[i + 2]), "=&v"(r[i + 3])
+        : "v"(a[i]), "v"(a[i + 1]), "v"(a[i + 2]), "v"(a[i + 3])
+        : "memory");
+#pragma unroll
+  for (; i + 2 <= N; i += 2)
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[i]), "=&v"(r[i + 1])
+                 : "v"(a[i]), "v"(a[i + 1])
+                 : "memory");
+#pragma unroll
+  for (; i < N; ++i)
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[i]) : "v"(a[i]) : "memory");
+}
+
 // ----------------------------------------------------------------------------- tiled kernel, 128-byte stages
 
 // The same tile and wave layout, with K staged 128 bytes (two MFMA K steps) at
@@ -359,23 +442,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS bases stay scalar
-  int tm, tn;
-  map_tile(blockIdx.x, tiles_m * tiles_n, tiles_m, group, tm, tn);
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int ntiles = tiles_m * tiles_n;
 
-  // DMA lanes: instruction i of wave w fills LDS rows (w*4 + i)*8 .. +8 of one
-  // operand; lane -> row lane / 8, slot lane % 8, which holds chunk
-  // slot ^ swz2(row). Rows past M or N re-read the last row (never stored).
+  // Persistent: workgroup b takes tiles b, b + G, b + 2G, ... (G = gridDim.x,
+  // a multiple of 8 whenever G < ntiles, so each id keeps the XCD that
+  // map_tile assumes and the tiles run in the order a one-tile-per-workgroup
+  // launch would dispatch them). Per tile: DMA lanes, instruction i of wave w
+  // filling LDS rows (w*4 + i)*8 .. +8 of one operand; lane -> row lane / 8,
+  // slot lane % 8, which holds chunk slot ^ swz2(row). Rows past M or N
+  // re-read the last row (never stored).
+  int m0 = 0, n0 = 0;
   uint32_t a_off[kDma2PerWave], b_off[kDma2PerWave];
+  __amdgpu_buffer_rsrc_t ra, rb;
+  auto setup = [&](int v) {
+    int tm, tn;
+    map_tile(v, ntiles, tiles_m, group, tm, tn);
+    m0 = tm * kTile;
+    n0 = tn * kTile;
+    // recomputed per tile from the lane id read afresh (mbcnt in volatile asm
+    // cannot be hoisted): kept across the tile loop, these per-lane offsets
+    // would hold registers the loop needs
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
-  for (int i = 0; i < kDma2PerWave; ++i) {
-    const int r = (wid * kDma2PerWave + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz2(r);
-    a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
-    b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
-  }
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
+    for (int i = 0; i < kDma2PerWave; ++i) {
+      const int r = (wid * kDma2PerWave + i) * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz2(r);
+      a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
+      b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
+    }
+    ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
+    rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
+  };
 
   // Fragment reads of K step t: row R = base + 16 i + lane % 16, chunk 4 t + lane / 16.
   const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
@@ -388,12 +486,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
     b_rd[t] = rrb * kSlice2 + 16 * (c ^ swz2(rrb));
   }
 
-  v4i acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
   // Stage S holds K steps 2S and 2S+1. Entering stage S, the fragments of step
   // 2S are in registers and stage S+1 is in flight. Step 2S reads the
   // fragments of step 2S+1 from the same stage and multiplies step 2S. Step
@@ -404,16 +496,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   // are clamped to the last stage; the final issues are harmless reloads.
   const int ns = K / kSlice2;
   const int last = (ns - 1) * kSlice2;
-  // in stage order: the waits count DMAs in issue order (see the 64-byte kernel)
-  issue_stage2(ra, lA0, a_off, 0, wid);
-  issue_stage2(rb, lB0, b_off, 0, wid);
-  memory_opaque();
-  issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
-  issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
-  Frags f0, f1;
-  __builtin_amdgcn_s_waitcnt(0x0F78);     // vmcnt(8): stage 0 landed
-  stage_barrier();
-  read_frags2(lA0, lB0, a_rd, b_rd, 0, f0);
+  auto prologue = [&]() {
+    // in stage order: the waits count DMAs in issue order (see the 64-byte kernel)
+    issue_stage2(ra, lA0, a_off, 0, wid);
+    issue_stage2(rb, lB0, b_off, 0, wid);
+    memory_opaque();
+    issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
+    issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
+  };
+  int v = blockIdx.x;
+  setup(v);
+  prologue();
+
+  for (;;) {
+    v4i acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    Frags f0, f1;
+    // vmcnt(8): stage 0 landed. Loads complete in issue order, so with at most
+    // 8 operations outstanding no load of stage 0 can be (the previous tile's
+    // stores, issued after these DMAs, are waited for as well).
+    __builtin_amdgcn_s_waitcnt(0x0F78);
+    stage_barrier();
+    {
+      // in asm: across the tile loop's back edge the compiler's own waits would
+      // also drain stage 1 and the previous tile's stores (vmcnt(0))
+      uint32_t addr[TI + TJ];
+      v4i r[TI + TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) addr[i] = lds_addr(lA0) + a_rd[0] + i * 16 * kSlice2;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) addr[TI + j] = lds_addr(lB0) + b_rd[0] + j * 16 * kSlice2;
+      lds_read_frags(r, addr);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) f0.a[i] = r[i];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) f0.b[j] = r[TI + j];
+    }
 
 #define SQ_STAGE(LA_CUR, LB_CUR, LA_NXT, LB_NXT)                                      \
   {                                                                                   \
@@ -431,26 +552,55 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
     interleave2(true);                                                                \
     ++s;                                                                              \
   }
-  int s = 0;
-  for (; s + 2 <= ns;) {
-    SQ_STAGE(lA0, lB0, lA1, lB1)
-    SQ_STAGE(lA1, lB1, lA0, lB0)
-  }
-  if (s < ns) SQ_STAGE(lA0, lB0, lA1, lB1)
-#undef SQ_STAGE
-  __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): no DMA into LDS outlives the loop
-
-  // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int m = m0 + wm + 16 * i + (lane & 15);
-    if (m >= M) continue;
-    const float xsm = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
-      if (n < N) store4<YDT>(y, N, m, n, acc[i][j], xsm, ws, bias);
+    int s = 0;
+    for (; s + 2 <= ns;) {
+      SQ_STAGE(lA0, lB0, lA1, lB1)
+      SQ_STAGE(lA1, lB1, lA0, lB0)
     }
+    if (s < ns) SQ_STAGE(lA0, lB0, lA1, lB1)
+#undef SQ_STAGE
+    __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): no DMA into LDS outlives the loop
+
+    // This tile's scales, loaded before the next tile's DMAs so that the
+    // epilogue waits for these loads only (a bias is read in the epilogue).
+    const int cm0 = m0, cn0 = n0;
+    float xsv[TI], wv[TJ][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = min(cm0 + wm + 16 * i + (lane & 15), M - 1);
+      xsv[i] = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int nn = min(cn0 + wn + 16 * j + 4 * (lane >> 4) + r, N - 1);
+        wv[j][r] = (YDT == SQ_DT_I32) ? 0.0f : ws[nn];
+      }
+
+    // Every wave is done reading the ring: the next tile's first two stages
+    // go out now and land while this tile's outputs are written.
+    stage_barrier();
+    const int vn = v + static_cast<int>(gridDim.x);
+    const bool more = vn < ntiles;
+    if (more) {
+      setup(vn);
+      prologue();
+    }
+
+    // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = cm0 + wm + 16 * i + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
+        if (n < N) store4_pre<YDT>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
+      }
+    }
+    if (!more) break;
+    v = vn;
   }
 }
 
@@ -607,38 +757,6 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
                                            0x00020000);
-}
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const int8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
-}
-
-// Fragment reads written in asm: at the top of the ring loop the compiler no
-// longer knows which stage each outstanding DMA writes and would drain them
-// all (vmcnt(0)) before a plain LDS read. The DMA data is already covered by
-// the explicit vmcnt wait ahead of the stage barrier; each asm statement waits
-// for its own reads before its outputs are used.
-template <int N>
-__device__ __forceinline__ void lds_read_frags(v4i (&r)[N], const uint32_t (&a)[N]) {
-  int i = 0;
-#pragma unroll
-  for (; i + 4 <= N; i += 4)
-    asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[i]), "=&v"(r[i + 1]), "=&v"(r[i + 2]), "=&v"(r[i + 3])
-        : "v"(a[i]), "v"(a[i + 1]), "v"(a[i + 2]), "v"(a[i + 3])
-        : "memory");
-#pragma unroll
-  for (; i + 2 <= N; i += 2)
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(r[i]), "=&v"(r[i + 1])
-                 : "v"(a[i]), "v"(a[i + 1])
-                 : "memory");
-#pragma unroll
-  for (; i < N; ++i)
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[i]) : "v"(a[i]) : "memory");
 }
 
 // ----------------------------------------------------------------------------- decode kernel, 128-byte segments
@@ -987,16 +1105,32 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
 #undef SQ_DECODE
 }
 
+// Workgroups of 512 threads of `kernel` resident on the device at once (all CUs
+// x occupancy), never below 8.
+inline hipError_t resident_tile_blocks(const void* kernel, int* out) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 512, 0);
+  *out = e == hipSuccess ? max(8, cus * max(per_cu, 1)) : 0;
+  return e;
+}
+
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) return launch_decode<YDT, false>(g, st);
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
-  if (g.K % kSlice2 == 0)
-    hipLaunchKernelGGL((k_gemm_tile<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
-                       g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
-  else
+  if (g.K % kSlice2 == 0) {
+    // persistent: at most one workgroup per resident slot, a multiple of 8 (one per XCD round)
+    const int ntiles = tiles_m * tiles_n;
+    int cap = 0;
+    if (hipError_t e = resident_tile_blocks(reinterpret_cast<const void*>(k_gemm_tile<YDT>), &cap)) return e;
+    const int grid = ntiles <= cap ? ntiles : (cap & ~7);
+    hipLaunchKernelGGL((k_gemm_tile<YDT>), dim3(grid), dim3(512), 0, st, g.xq, g.x_scale, g.wq, g.w_scale, g.bias,
+                       g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  } else
     hipLaunchKernelGGL((k_gemm_tile_k64<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
                        g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
   return hipGetLastError();
