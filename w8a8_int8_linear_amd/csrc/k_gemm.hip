@@ -89,12 +89,13 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int N, int m, int n
 // holds ws[n .. n+3], clamped to the last column): the same roundings, for an
 // epilogue that must not wait on memory issued after the scales. The bias, when
 // there is one, is read here.
-template <int YDT>
-__device__ __forceinline__ void store4_pre(void* __restrict__ y, int N, int m, int n, const v4i acc, float xs,
+template <int YDT, typename AccV = v4i>
+__device__ __forceinline__ void store4_pre(void* __restrict__ y, int N, int m, int n, const AccV acc, float xs,
                                            const float (&w)[4], const float* __restrict__ bias) {
   const int64_t off = static_cast<int64_t>(m) * N + n;
   const bool full = (n + 3 < N) && ((N & 3) == 0);
   if constexpr (YDT == SQ_DT_I32) {
+    static_assert(std::is_same_v<AccV, v4i>, "int32 output of an int32 accumulator");
     int* p = static_cast<int*>(y) + off;
     if (full) {
       *reinterpret_cast<int4*>(p) = make_int4(acc[0], acc[1], acc[2], acc[3]);
@@ -653,19 +654,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int tm, tn;
-  map_tile(blockIdx.x, tiles_m * tiles_n, tiles_m, group, tm, tn);
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int ntiles = tiles_m * tiles_n;
+  // persistent over tiles b, b + G, ..., as k_gemm_tile
+  int m0 = 0, n0 = 0;
   uint32_t a_off[kDma2PerWave], b_off[kDma2PerWave];
+  __amdgpu_buffer_rsrc_t ra, rb;
+  auto setup = [&](int v) {
+    int tm, tn;
+    map_tile(v, ntiles, tiles_m, group, tm, tn);
+    m0 = tm * kTile;
+    n0 = tn * kTile;
+    int ln;                                         // the lane id read afresh, as in k_gemm_tile
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
-  for (int i = 0; i < kDma2PerWave; ++i) {
-    const int r = (wid * kDma2PerWave + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz2(r);
-    a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
-    b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
-  }
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
+    for (int i = 0; i < kDma2PerWave; ++i) {
+      const int r = (wid * kDma2PerWave + i) * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz2(r);
+      a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
+      b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
+    }
+    ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
+    rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
+  };
   const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
   const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
   int a_rd[2], b_rd[2];
@@ -675,25 +685,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
     a_rd[t] = rra * kSlice2 + 16 * (c ^ swz2(rra));
     b_rd[t] = rrb * kSlice2 + 16 * (c ^ swz2(rrb));
   }
-  v4f acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int ns = K / kSlice2;
   const int last = (ns - 1) * kSlice2;
-  issue_stage2(ra, lA0, a_off, 0, wid);
-  issue_stage2(rb, lB0, b_off, 0, wid);
-  memory_opaque();
-  issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
-  issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
-  __builtin_amdgcn_s_waitcnt(0x0F78);     // vmcnt(8): stage 0 landed
-  stage_barrier();
-  v8i fb[TJ], a_cur;
+  auto prologue = [&]() {
+    issue_stage2(ra, lA0, a_off, 0, wid);
+    issue_stage2(rb, lB0, b_off, 0, wid);
+    memory_opaque();
+    issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
+    issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
+  };
+  int v = blockIdx.x;
+  setup(v);
+  prologue();
+
+  for (;;) {
+    v4f acc[TI][TJ];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) fb[j] = lds_frag8(lB0 + j * 16 * kSlice2, b_rd[0], b_rd[1]);
-  a_cur = lds_frag8(lA0, a_rd[0], a_rd[1]);
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    __builtin_amdgcn_s_waitcnt(0x0F78);     // vmcnt(8): stage 0 landed (see k_gemm_tile)
+    stage_barrier();
+    v8i fb[TJ], a_cur;
+    {
+      // in asm, as in k_gemm_tile: both K halves of the B blocks and of A block 0
+      uint32_t addr[2 * TJ + 2];
+      v4i r[2 * TJ + 2];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        addr[2 * j] = lds_addr(lB0) + j * 16 * kSlice2 + b_rd[0];
+        addr[2 * j + 1] = lds_addr(lB0) + j * 16 * kSlice2 + b_rd[1];
+      }
+      addr[2 * TJ] = lds_addr(lA0) + a_rd[0];
+      addr[2 * TJ + 1] = lds_addr(lA0) + a_rd[1];
+      lds_read_frags(r, addr);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) fb[j] = __builtin_shufflevector(r[2 * j], r[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      a_cur = __builtin_shufflevector(r[2 * TJ], r[2 * TJ + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 
 #define SQ_FP8_STAGE(LA, LB, LA_NXT, LB_NXT)                                                              \
   {                                                                                                      \
@@ -717,25 +747,43 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
     __builtin_amdgcn_sched_barrier(0);                                                                   \
     ++s;                                                                                                 \
   }
-  int s = 0;
-  for (; s + 2 <= ns;) {
-    SQ_FP8_STAGE(lA0, lB0, lA1, lB1)
-    SQ_FP8_STAGE(lA1, lB1, lA0, lB0)
-  }
-  if (s < ns) SQ_FP8_STAGE(lA0, lB0, lA1, lB1)
-#undef SQ_FP8_STAGE
-  __builtin_amdgcn_s_waitcnt(0x0070);     // no DMA into LDS outlives the loop
-
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int m = m0 + wm + 16 * i + (lane & 15);
-    if (m >= M) continue;
-    const float xsm = xs[m];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
-      if (n < N) store4<YDT>(y, N, m, n, acc[i][j], xsm, ws, bias);
+    int s = 0;
+    for (; s + 2 <= ns;) {
+      SQ_FP8_STAGE(lA0, lB0, lA1, lB1)
+      SQ_FP8_STAGE(lA1, lB1, lA0, lB0)
     }
+    if (s < ns) SQ_FP8_STAGE(lA0, lB0, lA1, lB1)
+#undef SQ_FP8_STAGE
+    __builtin_amdgcn_s_waitcnt(0x0070);     // no DMA into LDS outlives the loop
+
+    // this tile's scales before the next tile's DMAs, then the epilogue (as k_gemm_tile)
+    const int cm0 = m0, cn0 = n0;
+    float xsv[TI], wv[TJ][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) xsv[i] = xs[min(cm0 + wm + 16 * i + (lane & 15), M - 1)];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[j][r] = ws[min(cn0 + wn + 16 * j + 4 * (lane >> 4) + r, N - 1)];
+    stage_barrier();
+    const int vn = v + static_cast<int>(gridDim.x);
+    const bool more = vn < ntiles;
+    if (more) {
+      setup(vn);
+      prologue();
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = cm0 + wm + 16 * i + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
+        if (n < N) store4_pre<YDT, v4f>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
+      }
+    }
+    if (!more) break;
+    v = vn;
   }
 }
 
@@ -1144,7 +1192,11 @@ hipError_t launch_fp8_typed(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
-  hipLaunchKernelGGL((k_gemm_tile_fp8<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st,
+  const int ntiles = tiles_m * tiles_n;
+  int cap = 0;
+  if (hipError_t e = resident_tile_blocks(reinterpret_cast<const void*>(k_gemm_tile_fp8<YDT>), &cap)) return e;
+  const int grid = ntiles <= cap ? ntiles : (cap & ~7);
+  hipLaunchKernelGGL((k_gemm_tile_fp8<YDT>), dim3(grid), dim3(512), 0, st,
                      reinterpret_cast<const uint8_t*>(g.xq), g.x_scale, reinterpret_cast<const uint8_t*>(g.wq),
                      g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
   return hipGetLastError();
