@@ -62,6 +62,9 @@ def parse():
                         "exit; with --decode-sweep / --summarize-decode, the FP8 decode GEMMs instead")
     p.add_argument("--summarize-fp8", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --fp8 into a profiles/ table and exit")
+    p.add_argument("--prefill-sweep", action="store_true",
+                   help="time the prefill GEMMs of every workload (fp16 out) beside torch._int_mm (int32 out) "
+                        "and exit")
     return p.parse_args()
 
 
@@ -324,6 +327,55 @@ def summarize_decode(trace_dir, fp8=False):
 
 GRAN_CMD = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
             "python3 bench.py --granularities")
+
+
+def prefill_sweep():
+    """Prefill GEMMs of every workload's sites (fp16 out, with the dequantising epilogue) beside
+    torch._int_mm (the vendor library, raw int32 out): the best of three means of back-to-back launches."""
+    import torch
+    import w8a8_int8_linear_amd as sq
+    from synth import WORKLOADS
+
+    def best_ms(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) / n)
+        return best
+
+    g = torch.Generator(device="cpu").manual_seed(1)
+    for wl_id in sorted(WORKLOADS):
+        wl = WORKLOADS[wl_id]
+        m = max(wl.m)
+        if m <= 64:
+            continue                                       # decode shapes: --decode-sweep
+        for site in wl.sites:
+            n, k = site.n, site.k
+            xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, generator=g).cuda()
+            wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, generator=g).cuda()
+            xs = torch.rand(m, generator=g).cuda()
+            ws = torch.rand(n, generator=g).cuda()
+            y = torch.empty(m, n, dtype=torch.float16, device="cuda")
+            reps = 5 if m * n * k > 1e12 else 30
+            t = best_ms(lambda: sq.sq_w8a8_gemm(xq, xs, wq, ws, y=y, out_dtype=torch.float16), reps)
+            wt = wq.t()
+            tb = best_ms(lambda: torch._int_mm(xq, wt), reps)
+            ops = 2.0 * m * n * k
+            print(json.dumps({"workload": wl.name, "site": site.name, "mnk": [m, n, k],
+                              "tiles": -(-m // 256) * -(-n // 256), "ms": round(t, 4),
+                              "TOPS": round(ops / t / 1e9, 1), "int_mm_ms": round(tb, 4),
+                              "int_mm_TOPS": round(ops / tb / 1e9, 1)}), flush=True)
+            del xq, wq, y
+            torch.cuda.empty_cache()
 
 
 def median_ms(torch, fn, n):
@@ -783,6 +835,9 @@ def main():
         sys.exit(2)
     if args.decode_sweep:
         decode_sweep(args.fp8)
+        return
+    if args.prefill_sweep:
+        prefill_sweep()
         return
     if args.granularities:
         granularity_sweep(args)
