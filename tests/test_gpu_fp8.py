@@ -270,6 +270,35 @@ def test_fp8_gemm_decode_every_token_count(m, n):
     assert np.all(err <= tol), f"max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3g}"
 
 
+# More tiles than resident workgroups: the FP8 prefill kernel's workgroups loop over several tiles,
+# with ragged last tile-rows and -columns; sampled positions cover every tile.
+@pytest.mark.parametrize("shape", [(2100, 8000, 256), (4097, 9000, 384)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_gemm_persistent_grid(shape):
+    m, n, k = shape
+    xq = _codes((m, k), 11 + m, 40.0)
+    wq = _codes((n, k), 13 + n, 0.5)
+    rng = np.random.default_rng(m + n)
+    xs = (rng.uniform(0.5, 2, m) * 1e-2).astype(F32)
+    ws = (rng.uniform(0.5, 2, n) * 1e-3).astype(F32)
+    bias = rng.standard_normal(n).astype(F32)
+    y = sq.sq_fp8_gemm(torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda(), torch.from_numpy(wq).cuda(),
+                       torch.from_numpy(ws).cuda(), torch.from_numpy(bias).cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tm, tn = np.meshgrid(np.arange(-(-m // 256)), np.arange(-(-n // 256)), indexing="ij")
+    mi = np.concatenate([np.minimum(tm.ravel() * 256 + rng.integers(0, 256, tm.size), m - 1),
+                         rng.integers(0, m, 2000), [0, m - 1, m - 1, 0]])
+    ni = np.concatenate([np.minimum(tn.ravel() * 256 + rng.integers(0, 256, tn.size), n - 1),
+                         rng.integers(0, n, 2000), [0, n - 1, 0, n - 1]])
+    acc, tol_acc = fp8_gemm_tolerance(xq, wq, mi, ni)
+    scale = xs.astype(np.float64)[mi] * ws.astype(np.float64)[ni]
+    b = bias.astype(np.float64)[ni]
+    ref = acc * scale + b
+    tol = (tol_acc * scale * (1 + 2.0 ** -20) + ((np.abs(acc) + tol_acc) * scale + np.abs(b)) * 3 * 2.0 ** -24
+           + np.abs(ref) * 2.0 ** -24 + 2.0 ** -24)
+    err = np.abs(host(y)[mi, ni].astype(np.float64) - ref)
+    assert np.all(err <= tol), f"max excess {np.max(err - tol):.3g}"
+
+
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_fp8_gemm_dequantised_output(out):
     m, n, k = 300, 520, 1280

@@ -213,6 +213,42 @@ def test_gemm_decode_every_token_count(m, nk):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
 
 
+
+# More tiles than resident workgroups: the prefill kernel's workgroups loop over several tiles (each
+# tile's epilogue overlapping the next tile's first stages), with ragged last tile-rows and -columns.
+# Every tile-row is sampled (every 16th row and the edges) against all columns.
+PERSIST_SHAPES = [(2100, 8000, 256), (4097, 16385, 128), (1100, 30000, 384)]
+
+
+def _persist_rows(m):
+    return np.unique(np.r_[np.arange(0, m, 16), [255, 256, m - 2, m - 1]])
+
+
+@pytest.mark.parametrize("mnk", PERSIST_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_persistent_grid_accumulators(mnk):
+    m, n, k = mnk
+    xq, wq = rand_int8((m, k), 800 + m), rand_int8((n, k), 900 + n)
+    acc = sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rows = _persist_rows(m)
+    ref = O.int_gemm(xq.numpy()[rows], wq.numpy())
+    got = host(acc)[rows].astype(np.int64)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
+def test_gemm_persistent_grid_dequant_with_bias(out):
+    m, n, k = 2100, 8000, 256
+    xq, wq = rand_int8((m, k), 810), rand_int8((n, k), 910)
+    xs, ws = rand_positive(m, 820, 1e-3, 0.5), rand_positive(n, 920, 1e-4, 0.05)
+    b = rand_tokens(1, n, "f32", 930)[0]
+    y = sq.sq_w8a8_gemm(cuda(xq), cuda(xs), cuda(wq), cuda(ws), cuda(b), out_dtype=OUT_DT[out])
+    torch.cuda.synchronize()
+    rows = _persist_rows(m)
+    acc = O.int_gemm(xq.numpy()[rows], wq.numpy())
+    out_ref, v32 = O.dequantize(acc, xs.numpy()[rows], ws.numpy(), b.numpy(), out)
+    check_output(host(y)[rows], out_ref, v32, out, label=f"{out}/{m}x{n}x{k}")
+
 def test_gemm_int32_range_at_max_k():
     k = sq.SQ_K_MAX
     for m in [3, 70]:                                        # GEMV and tiled kernels
