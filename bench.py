@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--prefill-sweep", action="store_true",
                    help="time the prefill GEMMs of every workload (fp16 out) beside torch._int_mm (int32 out) "
                         "and exit")
+    p.add_argument("--summarize-prefill", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace of --prefill-sweep into a profiles/ table and exit")
     return p.parse_args()
 
 
@@ -334,7 +336,6 @@ def prefill_sweep():
     torch._int_mm (the vendor library, raw int32 out): the best of three means of back-to-back launches."""
     import torch
     import w8a8_int8_linear_amd as sq
-    from synth import WORKLOADS
 
     def best_ms(fn, n):
         for _ in range(3):
@@ -353,29 +354,81 @@ def prefill_sweep():
         return best
 
     g = torch.Generator(device="cpu").manual_seed(1)
+    for wl_name, site_name, m, n, k in prefill_shapes():       # decode shapes (M <= 64): --decode-sweep
+        xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, generator=g).cuda()
+        wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, generator=g).cuda()
+        xs = torch.rand(m, generator=g).cuda()
+        ws = torch.rand(n, generator=g).cuda()
+        y = torch.empty(m, n, dtype=torch.float16, device="cuda")
+        reps = 5 if m * n * k > 1e12 else 30
+        t = best_ms(lambda: sq.sq_w8a8_gemm(xq, xs, wq, ws, y=y, out_dtype=torch.float16), reps)
+        wt = wq.t()
+        tb = best_ms(lambda: torch._int_mm(xq, wt), reps)
+        ops = 2.0 * m * n * k
+        print(json.dumps({"workload": wl_name, "site": site_name, "mnk": [m, n, k],
+                          "tiles": -(-m // 256) * -(-n // 256), "ms": round(t, 4),
+                          "TOPS": round(ops / t / 1e9, 1), "int_mm_ms": round(tb, 4),
+                          "int_mm_TOPS": round(ops / tb / 1e9, 1)}), flush=True)
+        del xq, wq, y
+        torch.cuda.empty_cache()
+
+
+PREFILL_CMD = "rocprofv3 --kernel-trace -d <dir> -o run --output-format csv -- python3 bench.py --prefill-sweep"
+
+
+def prefill_shapes():
+    """(workload, site, m, n, k) of every prefill GEMM, in --prefill-sweep order."""
+    from synth import WORKLOADS
+    out = []
     for wl_id in sorted(WORKLOADS):
         wl = WORKLOADS[wl_id]
         m = max(wl.m)
-        if m <= 64:
-            continue                                       # decode shapes: --decode-sweep
-        for site in wl.sites:
-            n, k = site.n, site.k
-            xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, generator=g).cuda()
-            wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, generator=g).cuda()
-            xs = torch.rand(m, generator=g).cuda()
-            ws = torch.rand(n, generator=g).cuda()
-            y = torch.empty(m, n, dtype=torch.float16, device="cuda")
-            reps = 5 if m * n * k > 1e12 else 30
-            t = best_ms(lambda: sq.sq_w8a8_gemm(xq, xs, wq, ws, y=y, out_dtype=torch.float16), reps)
-            wt = wq.t()
-            tb = best_ms(lambda: torch._int_mm(xq, wt), reps)
-            ops = 2.0 * m * n * k
-            print(json.dumps({"workload": wl.name, "site": site.name, "mnk": [m, n, k],
-                              "tiles": -(-m // 256) * -(-n // 256), "ms": round(t, 4),
-                              "TOPS": round(ops / t / 1e9, 1), "int_mm_ms": round(tb, 4),
-                              "int_mm_TOPS": round(ops / tb / 1e9, 1)}), flush=True)
-            del xq, wq, y
-            torch.cuda.empty_cache()
+        if m > 64:
+            out += [(wl.name, site.name, m, site.n, site.k) for site in wl.sites]
+    return out
+
+
+def summarize_prefill(trace_dir):
+    """Per-shape durations of this library's GEMM in a --prefill-sweep kernel trace. Dispatches are
+    taken in start order; each shape's launches form one run of GEMM-kernel dispatches, ended by the
+    vendor library's kernels that the sweep times next."""
+    import csv
+    import glob
+    import statistics
+    hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    rows = sorted(csv.DictReader(open(hits[0])), key=lambda r: int(r["Start_Timestamp"]))
+    runs, cur = [], None
+    for r in rows:
+        if "sq::k_gemm" in r["Kernel_Name"]:
+            if cur is None:
+                wg = int(r.get("Workgroup_Size_X") or 1)
+                cur = {"name": r["Kernel_Name"].split("(")[0].replace("void ", ""),
+                       "grid": int(r["Grid_Size_X"]) // wg, "wg": wg, "ns": []}
+                runs.append(cur)
+            cur["ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        elif "sq::" not in r["Kernel_Name"]:
+            cur = None
+    shapes = prefill_shapes()
+    if len(runs) != len(shapes):
+        raise SystemExit(f"{len(runs)} runs of GEMM dispatches for {len(shapes)} shapes")
+    lines = ["# Prefill GEMM kernel durations (rocprofv3 kernel trace): every workload's prefill sites, fp16 out",
+             "", f"Command: `{PREFILL_CMD}`, then `python bench.py --summarize-prefill <dir>`.", "",
+             "Random int8 operands; every launch of the sweep (warm-up included), back to back. The grid is "
+             "one workgroup per 256x256 tile, or (up to 16 tiles per resident workgroup) one per CU looping "
+             "over the tiles.", "",
+             "| workload | site | M x N x K | kernel | workgroups x threads | launches | median ms | min ms | "
+             "TOPS (median) |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (wl, site, m, n, k), run in zip(shapes, runs):
+        med = statistics.median(run["ns"]) / 1e6
+        lines.append(f"| {wl} | {site} | {m} x {n} x {k} | `{run['name']}` | {run['grid']} x {run['wg']} | "
+                     f"{len(run['ns'])} | {med:.4f} | {min(run['ns']) / 1e6:.4f} | "
+                     f"{2.0 * m * n * k / med / 1e9:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "prefill_gemm_all_workloads.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def median_ms(torch, fn, n):
@@ -828,6 +881,9 @@ def main():
         return
     if args.summarize_fp8:
         summarize_fp8(args.summarize_fp8)
+        return
+    if args.summarize_prefill:
+        summarize_prefill(args.summarize_prefill)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",

@@ -94,3 +94,24 @@ def test_decode_bytes_counts_weights_tokens_scales_and_output():
     # N*K weight codes + M*K token codes + 4 (M + N) scale bytes + 2 M N fp16 outputs
     assert bench.decode_bytes(1, 9216) == 9216 * 9216 + 9216 + 4 * (1 + 9216) + 2 * 9216
     assert bench.decode_bytes(64, 36864, 9216) == 36864 * 9216 + 64 * 9216 + 4 * (64 + 36864) + 2 * 64 * 36864
+
+
+def test_prefill_summary_splits_runs_at_the_vendor_kernels(scratch_root):
+    header = ["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"]
+    rows, t = [], 0
+    shapes = bench.prefill_shapes()
+    for i, _ in enumerate(shapes):
+        for ms in (0.3, 0.1, 0.2):                                 # ours: median 0.2 ms (+ i)
+            rows.append(["void sq::k_gemm_tile<1>(...)", 256, t, t + int((ms + i) * 1e6)])
+            t += 20_000_000
+        for _ in range(2):                                         # the vendor library's launches
+            rows.append(["Cijk_Ailk_Bljk_I8II_BH(...)", 1024, t, t + 1_000_000])
+            t += 20_000_000
+    _write_csv(scratch_root / "pf" / "run_kernel_trace.csv", header, rows[::-1])    # any file order
+    bench.summarize_prefill(str(scratch_root / "pf"))
+    text = (scratch_root / "profiles" / "prefill_gemm_all_workloads.md").read_text()
+    body = [ln for ln in text.splitlines() if ln.startswith("| ") and "`sq::" in ln]
+    assert len(body) == len(shapes)
+    for i, ln in enumerate(body):
+        assert f"| 3 | {0.2 + i:.4f} | {0.1 + i:.4f} |" in ln
+    assert "Cijk" not in text
