@@ -16,9 +16,9 @@
 //    stages in flight during each epilogue. k_gemm_tile_k64 is the same tile
 //    with 64-byte slices in a 4-stage ring, for K % 128 == 64, one tile per
 //    workgroup.
-//  * k_gemv (up to 4 tokens, vector ALUs) and k_gemm_decode (5..64 tokens,
-//    MFMA) -- decode shapes, bound by streaming wq from HBM (described at the
-//    kernels).
+//  * k_gemv (up to 4 tokens at N >= 16384, vector ALUs) and k_gemm_decode
+//    (the other shapes up to 64 tokens, MFMA) -- decode shapes, bound by
+//    streaming wq from HBM (described at the kernels).
 //
 // MFMA operand order: the A operand (rows = lane % 16) carries 16 rows of wq and
 // the B operand (columns = lane % 16) 16 rows of xq, so the 16x16 result tile
@@ -1118,13 +1118,15 @@ __global__ __launch_bounds__(256) void k_gemv(const int8_t* __restrict__ xq, con
 
 namespace {
 
-// Decode shapes (M <= 64). INT8 with up to 4 tokens: the vector-ALU GEMV, 16
-// channels per workgroup (gfx950 has no FP8 dot product on the vector ALUs, so
-// FP8 always takes the MFMA kernel). Otherwise the MFMA decode kernel with up
-// to 9 channel tiles per workgroup, so that each token segment serves many
-// weight tiles (3 at small N: 48-channel strips put 192 workgroups on the
-// CUs where 64-channel strips put 144, 10-11% faster at 8-32 tokens).
-// Measured on K = 9216, N = 9216 / 36864.
+// Decode shapes (M <= 64). INT8 with up to 4 tokens at N >= 16384: the
+// vector-ALU GEMV, 16 channels per workgroup (6.8 TB/s at N = 36864, where the
+// MFMA kernel reaches 6.5). Otherwise the MFMA decode kernel (gfx950 has no
+// FP8 dot product on the vector ALUs, so FP8 always takes it) with up to 9
+// channel tiles per workgroup, so that each token segment serves many weight
+// tiles. At smaller N, 3 tiles: 48-channel strips put 192 workgroups on the
+// CUs where 64-channel strips put 144 (10-11% faster at 8-32 tokens), and at
+// N = 9216 this kernel beats the GEMV at 1-4 tokens as well (15.9-16.2
+// against 16.9-17.5 us). Measured on K = 9216, N = 9216 / 36864.
 template <int YDT, bool FP8>
 hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
   const int mt = (g.M + 15) / 16;
@@ -1135,7 +1137,7 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
                        g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
     return hipGetLastError();                                                                                \
   }
-  if constexpr (!FP8) {
+  if (!FP8 && wide) {
     if (g.M == 1) SQ_DECODE((k_gemv<1, 3, YDT>), 16)
     if (g.M == 2) SQ_DECODE((k_gemv<2, 3, YDT>), 16)
     if (g.M <= 4) SQ_DECODE((k_gemv<4, 2, YDT>), 16)
