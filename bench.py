@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--prefill-sweep", action="store_true",
                    help="time the prefill GEMMs of every workload (fp16 out) beside torch._int_mm (int32 out) "
                         "and exit")
+    p.add_argument("--summarize-decode-counters", metavar="PMC_DIR",
+                   help="turn a rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
+                        "SQ_LDS_BANK_CONFLICT run of --decode-sweep into a profiles/ table and exit")
     p.add_argument("--summarize-prefill", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace of --prefill-sweep into a profiles/ table and exit")
     return p.parse_args()
@@ -289,6 +292,50 @@ def decode_sweep(fp8=False):
             del xq, y
         del ws
         torch.cuda.empty_cache()
+
+
+DEC_PMC = ("SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT")
+
+
+def summarize_decode_counters(pmc_dir):
+    """LDS counters of the decode kernels in a --pmc run of --decode-sweep: per kernel instance, the
+    shares of wave cycles spent waiting on LDS instructions and issuing them, summed over the
+    instance's dispatches (SQ_LDS_BANK_CONFLICT counts the LDS unit's stall cycles, not wave
+    cycles, so it is not turned into a share)."""
+    import csv
+    import glob
+    from collections import defaultdict
+    hits = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no counter collection under {pmc_dir}")
+    tot = defaultdict(lambda: defaultdict(float))
+    calls = defaultdict(set)
+    for r in csv.DictReader(open(hits[0])):
+        name = r["Kernel_Name"]
+        if "sq::k_gemm_decode" not in name and "sq::k_gemv" not in name:
+            continue
+        grid = int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+        wg = int(r.get("Workgroup_Size") or r.get("Workgroup_Size_X") or 1)
+        key = (name.split("(")[0].replace("void ", ""), grid // wg)
+        tot[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        calls[key].add(r["Dispatch_Id"])
+    cmd = ("rocprofv3 --pmc " + " ".join(DEC_PMC) + " -d <dir> -o run --output-format csv -- "
+           "python3 bench.py --decode-sweep")
+    lines = ["# Decode GEMM LDS counters (rocprofv3 --pmc): OPT-66B width, K = 9216, INT8", "",
+             f"Command: `{cmd}`, then `python bench.py --summarize-decode-counters <dir>`.", "",
+             "Summed over each kernel instance's dispatches (every token count it serves, warm-up included). "
+             "Both columns are shares of all wave cycles (SQ_WAVE_CYCLES). SQ_LDS_BANK_CONFLICT, collected "
+             "in the same run, counts the LDS unit's stall cycles rather than wave cycles and is not shown.",
+             "", "| kernel | workgroups | dispatches | LDS wait / wave cycles | LDS active / wave cycles |"
+             "", "|---|---|---|---|---|"]
+    for key in sorted(tot, key=lambda k: (k[1], k[0])):
+        c = tot[key]
+        wc = max(c["SQ_WAVE_CYCLES"], 1.0)
+        lines.append(f"| `{key[0]}` | {key[1]} | {len(calls[key])} | {c['SQ_WAIT_INST_LDS'] / wc:.3f} | "
+                     f"{c['SQ_ACTIVE_INST_LDS'] / wc:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "decode_gemm_lds_counters_opt66b_k9216.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_decode(trace_dir, fp8=False):
@@ -881,6 +928,9 @@ def main():
         return
     if args.summarize_fp8:
         summarize_fp8(args.summarize_fp8)
+        return
+    if args.summarize_decode_counters:
+        summarize_decode_counters(args.summarize_decode_counters)
         return
     if args.summarize_prefill:
         summarize_prefill(args.summarize_prefill)
