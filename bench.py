@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--summarize-decode-counters", metavar="PMC_DIR",
                    help="turn a rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
                         "SQ_LDS_BANK_CONFLICT run of --decode-sweep into a profiles/ table and exit")
+    p.add_argument("--summarize-ln-counters", metavar="PMC_DIR",
+                   help="turn a rocprofv3 --pmc SQ_INSTS_VALU GRBM_GUI_ACTIVE run of this benchmark into a "
+                        "profiles/ table of the LayerNorm quantiser's vector-ALU issue and exit")
     p.add_argument("--summarize-prefill", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace of --prefill-sweep into a profiles/ table and exit")
     return p.parse_args()
@@ -334,6 +337,44 @@ def summarize_decode_counters(pmc_dir):
         lines.append(f"| `{key[0]}` | {key[1]} | {len(calls[key])} | {c['SQ_WAIT_INST_LDS'] / wc:.3f} | "
                      f"{c['SQ_ACTIVE_INST_LDS'] / wc:.3f} |")
     with open(os.path.join(ROOT, "profiles", "decode_gemm_lds_counters_opt66b_k9216.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_ln_counters(pmc_dir, m=8192, k=20480):
+    """Vector-ALU issue of the LayerNorm quantiser (MT-NLG width, 8192 x 20480 fp16) per dispatch:
+    SQ_INSTS_VALU counts wave instructions over the device, GRBM_GUI_ACTIVE the busy cycles summed over
+    the XCDs. Lane instructions per element = 64 x instructions / (M K); a CU issues at most one VALU
+    wave instruction per cycle (four SIMDs, four cycles each), so the issue share is instructions over
+    CU cycles."""
+    import csv
+    import glob
+    from collections import defaultdict
+    hits = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no counter collection under {pmc_dir}")
+    per = defaultdict(dict)
+    for r in csv.DictReader(open(hits[0])):
+        if "sq::k_norm_quant<sq::f16_t, 1," in r["Kernel_Name"]:
+            d = per[int(r["Dispatch_Id"])]
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        raise SystemExit("no LayerNorm quantiser dispatch in the run")
+    cmd = ("rocprofv3 --pmc SQ_INSTS_VALU GRBM_GUI_ACTIVE -d <dir> -o run --output-format csv -- "
+           "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline")
+    lines = ["# LayerNorm quantiser vector-ALU issue (rocprofv3 --pmc): MT-NLG width, 8192 x 20480 fp16", "",
+             f"Command: `{cmd}`, then `python bench.py --summarize-ln-counters <dir>`.", "",
+             "Kernel `sq::k_norm_quant<sq::f16_t, 1, 5, 512, 0>` (LayerNorm, per-token INT8 steps). Clock = "
+             "GRBM_GUI_ACTIVE / 8 XCDs / duration; issue share = SQ_INSTS_VALU / (256 CUs x cycles).", "",
+             "| dispatch | ms | clock GHz | VALU lane instructions per element | VALU issue share |",
+             "|---|---|---|---|---|"]
+    for i, (_, d) in enumerate(sorted(per.items())):
+        cyc = d["GRBM_GUI_ACTIVE"] / N_XCD
+        lines.append(f"| {'warm-up' if i == 0 and len(per) > 1 else 'timed'} | {d['ns'] / 1e6:.4f} | "
+                     f"{cyc / d['ns']:.2f} | {64.0 * d['SQ_INSTS_VALU'] / (m * k):.1f} | "
+                     f"{d['SQ_INSTS_VALU'] / (N_CU * cyc):.2f} |")
+    with open(os.path.join(ROOT, "profiles", "norm_quant_layernorm_valu_mtnlg530b.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -931,6 +972,9 @@ def main():
         return
     if args.summarize_decode_counters:
         summarize_decode_counters(args.summarize_decode_counters)
+        return
+    if args.summarize_ln_counters:
+        summarize_ln_counters(args.summarize_ln_counters)
         return
     if args.summarize_prefill:
         summarize_prefill(args.summarize_prefill)
