@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--workload", type=int, default=5)
     p.add_argument("--m", type=int, default=None, help="token count (workloads with several)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true", help="leave out the decode GEMM block")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration runs)")
@@ -63,8 +64,7 @@ def parse():
     p.add_argument("--summarize-fp8", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --fp8 into a profiles/ table and exit")
     p.add_argument("--prefill-sweep", action="store_true",
-                   help="time the prefill GEMMs of every workload (fp16 out) beside torch._int_mm (int32 out) "
-                        "and exit")
+                   help="time the prefill GEMMs of every workload (fp16 out) and exit")
     p.add_argument("--summarize-decode-counters", metavar="PMC_DIR",
                    help="turn a rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
                         "SQ_LDS_BANK_CONFLICT run of --decode-sweep into a profiles/ table and exit")
@@ -297,6 +297,61 @@ def decode_sweep(fp8=False):
         torch.cuda.empty_cache()
 
 
+DEC_BLOCK_MS = [1, 8, 32, 64]                 # the OPT-66B decode token counts
+
+
+def decode_block(torch, sq, replays=5):
+    """Decode GEMMs (K = 9216, N in {9216, 36864}, 1/8/32/64 tokens, fp16 out) for the default JSON
+    line. Per shape, one HIP graph launches the GEMM once per weight copy (copies totalling >= 600 MB
+    rotate, so no launch finds its weights in the 256 MB MALL); the graph is replayed between two HIP
+    events on the stream the library launches on, and the per-launch time is the replay's time over
+    the number of launches (kernel time plus the graph's dispatch gap)."""
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    out = []
+    for n in DEC_NS:
+        copies = max(2, -(-600_000_000 // (n * DEC_K)))
+        ws = [torch.randint(-127, 128, (n, DEC_K), dtype=torch.int8, device="cuda", generator=gen)
+              for _ in range(copies)]
+        wsc = torch.rand(n, device="cuda", generator=gen) * 0.01
+        for m in DEC_BLOCK_MS:
+            xq = torch.randint(-127, 128, (m, DEC_K), dtype=torch.int8, device="cuda", generator=gen)
+            xs = torch.rand(m, device="cuda", generator=gen) * 0.01
+            y = torch.empty(m, n, dtype=torch.float16, device="cuda")
+
+            def launches():
+                for w in ws:
+                    sq.sq_w8a8_gemm(xq, xs, w, wsc, y=y, out_dtype=torch.float16)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                launches()                                     # warm-up outside the capture
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                launches()
+            graph.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(replays):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                graph.replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / copies)
+            ts.sort()
+            us = ts[len(ts) // 2]
+            gbs = decode_bytes(m, n) / us / 1e3
+            out.append({"tokens": m, "N": n, "K": DEC_K, "us": round(us, 2), "GBps": round(gbs, 1),
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+            del graph, xq, y
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
 DEC_PMC = ("SQ_WAVE_CYCLES", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT")
 
 
@@ -419,18 +474,25 @@ GRAN_CMD = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format cs
             "python3 bench.py --granularities")
 
 
+PREFILL_WARM, PREFILL_TIMES = 3, 3
+
+
+def prefill_reps(m, n, k):
+    return 5 if m * n * k > 1e12 else 30
+
+
 def prefill_sweep():
-    """Prefill GEMMs of every workload's sites (fp16 out, with the dequantising epilogue) beside
-    torch._int_mm (the vendor library, raw int32 out): the best of three means of back-to-back launches."""
+    """Prefill GEMMs of every workload's sites (fp16 out, with the dequantising epilogue): the best of
+    three means of back-to-back launches, after PREFILL_WARM untimed launches."""
     import torch
     import w8a8_int8_linear_amd as sq
 
     def best_ms(fn, n):
-        for _ in range(3):
+        for _ in range(PREFILL_WARM):
             fn()
         torch.cuda.synchronize()
         best = float("inf")
-        for _ in range(3):
+        for _ in range(PREFILL_TIMES):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
@@ -448,15 +510,11 @@ def prefill_sweep():
         xs = torch.rand(m, generator=g).cuda()
         ws = torch.rand(n, generator=g).cuda()
         y = torch.empty(m, n, dtype=torch.float16, device="cuda")
-        reps = 5 if m * n * k > 1e12 else 30
-        t = best_ms(lambda: sq.sq_w8a8_gemm(xq, xs, wq, ws, y=y, out_dtype=torch.float16), reps)
-        wt = wq.t()
-        tb = best_ms(lambda: torch._int_mm(xq, wt), reps)
+        t = best_ms(lambda: sq.sq_w8a8_gemm(xq, xs, wq, ws, y=y, out_dtype=torch.float16), prefill_reps(m, n, k))
         ops = 2.0 * m * n * k
         print(json.dumps({"workload": wl_name, "site": site_name, "mnk": [m, n, k],
                           "tiles": -(-m // 256) * -(-n // 256), "ms": round(t, 4),
-                          "TOPS": round(ops / t / 1e9, 1), "int_mm_ms": round(tb, 4),
-                          "int_mm_TOPS": round(ops / tb / 1e9, 1)}), flush=True)
+                          "TOPS": round(ops / t / 1e9, 1)}), flush=True)
         del xq, wq, y
         torch.cuda.empty_cache()
 
@@ -478,29 +536,28 @@ def prefill_shapes():
 
 def summarize_prefill(trace_dir):
     """Per-shape durations of this library's GEMM in a --prefill-sweep kernel trace. Dispatches are
-    taken in start order; each shape's launches form one run of GEMM-kernel dispatches, ended by the
-    vendor library's kernels that the sweep times next."""
+    taken in start order; each shape's launches are the next PREFILL_WARM + PREFILL_TIMES * reps
+    GEMM dispatches."""
     import csv
     import glob
     import statistics
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no kernel trace under {trace_dir}")
-    rows = sorted(csv.DictReader(open(hits[0])), key=lambda r: int(r["Start_Timestamp"]))
-    runs, cur = [], None
-    for r in rows:
-        if "sq::k_gemm" in r["Kernel_Name"]:
-            if cur is None:
-                wg = int(r.get("Workgroup_Size_X") or 1)
-                cur = {"name": r["Kernel_Name"].split("(")[0].replace("void ", ""),
-                       "grid": int(r["Grid_Size_X"]) // wg, "wg": wg, "ns": []}
-                runs.append(cur)
-            cur["ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        elif "sq::" not in r["Kernel_Name"]:
-            cur = None
+    rows = sorted((r for r in csv.DictReader(open(hits[0])) if "sq::k_gemm" in r["Kernel_Name"]),
+                  key=lambda r: int(r["Start_Timestamp"]))
     shapes = prefill_shapes()
-    if len(runs) != len(shapes):
-        raise SystemExit(f"{len(runs)} runs of GEMM dispatches for {len(shapes)} shapes")
+    counts = [PREFILL_WARM + PREFILL_TIMES * prefill_reps(m, n, k) for _, _, m, n, k in shapes]
+    if len(rows) != sum(counts):
+        raise SystemExit(f"{len(rows)} GEMM dispatches, expected {sum(counts)}")
+    runs, at = [], 0
+    for c in counts:
+        rs = rows[at:at + c]
+        at += c
+        wg = int(rs[0].get("Workgroup_Size_X") or 1)
+        runs.append({"name": rs[0]["Kernel_Name"].split("(")[0].replace("void ", ""),
+                     "grid": int(rs[0]["Grid_Size_X"]) // wg, "wg": wg,
+                     "ns": [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs]})
     lines = ["# Prefill GEMM kernel durations (rocprofv3 kernel trace): every workload's prefill sites, fp16 out",
              "", f"Command: `{PREFILL_CMD}`, then `python bench.py --summarize-prefill <dir>`.", "",
              "Random int8 operands; every launch of the sweep (warm-up included), back to back. The grid is "
@@ -912,46 +969,73 @@ def kernel_report(timer, wl, sites):
 
 
 def cpu_baseline(wl, budget_s):
-    """The oracle on a bounded sample of the workload: every site's full chain on a few
-    tokens and output channels at the full K. Returns throughput in GEMM TOPS."""
+    """The oracle on a bounded sample of the workload, stage by stage, on the host cores: calibration,
+    fold, norm + quantise (GB/s of the stage's algorithmic bytes) and the INT8 GEMM with its epilogue
+    (TOPS). BLAS threads are set to the cores this process may use (OMP_NUM_THREADS when set); all
+    else is single-threaded numpy and Python. The sample is every site of the workload at its full K
+    (the first site's norm, activations and weights), with few enough rows that the whole leg takes
+    about budget_s seconds."""
     import numpy as np
     import oracle as O
     from synth import site_inputs, to_numpy
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
-    m_s, n_s, cal_s = 4, 256, 16
-    elapsed = 0.0
-    ops = 0.0
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    esize = {"f32": 4, "f16": 2, "bf16": 2}[wl.dtype]
+    osize = {"f32": 4, "f16": 2, "bf16": 2}[wl.out_dtype]
+    m_s, n_s, cal_s, gm_s = 8, 256, 16, 256           # rows of each stage's sample
+    acc = {k: [0.0, 0.0] for k in ("calibrate", "fold", "norm_quant", "gemm")}   # seconds, work
     reps = 0
-    while True:
-        for si, site in enumerate(wl.sites):
-            inp = site_inputs(wl.id, si, m=m_s, device="cpu", w_rows=n_s)
-            x = to_numpy(inp["x"])
-            x_cal = to_numpy(inp["x_cal"][:cal_s])
-            w = to_numpy(inp["w"])
-            gamma = None if inp["gamma"] is None else inp["gamma"].numpy()
-            beta = None if inp["beta"] is None else inp["beta"].numpy()
-            t0 = time.perf_counter()
-            O.w8a8_linear(x, x_cal, w, wl.dtype, site.norm, wl.alpha, gamma, beta, EPS, wl.out_dtype)
-            elapsed += time.perf_counter() - t0
-            ops += 2.0 * m_s * n_s * site.k
-        reps += 1
-        if elapsed >= budget_s or reps >= 50:
-            break
-    sample = (f"{reps} x every site's full oracle chain on {m_s} tokens, {cal_s} calibration tokens and the first "
-              f"{n_s} output channels at full K")
+    t_start = time.perf_counter()
+    with threadpool_limits(limits=threads):
+        while True:
+            for si, site in enumerate(wl.sites):
+                k = site.k
+                inp = site_inputs(wl.id, si, m=max(m_s, gm_s), device="cpu", w_rows=n_s)
+                x = to_numpy(inp["x"])
+                x_cal = to_numpy(inp["x_cal"][:cal_s])
+                w = to_numpy(inp["w"])
+                gamma = None if inp["gamma"] is None else inp["gamma"].numpy()
+                beta = None if inp["beta"] is None else inp["beta"].numpy()
+                nparams = {"none": 1, "layernorm": 2, "rmsnorm": 1}[site.norm]
+                t0 = time.perf_counter()
+                a, _ = O.calibrate(x_cal, wl.dtype, site.norm, gamma, beta, EPS)
+                t1 = time.perf_counter()
+                f = O.fold(a, w, wl.dtype, wl.alpha, O.EPS_FOLD, site.norm, gamma, beta)
+                t2 = time.perf_counter()
+                xq, xs, _ = O.norm_quant(x[:m_s], wl.dtype, site.norm, f["gamma_f"], f["beta_f"], EPS)
+                t3 = time.perf_counter()
+                xq_g = np.resize(xq, (gm_s, k))              # the GEMM stage on gm_s token rows
+                xs_g = np.resize(xs, gm_s)
+                O.dequantize(O.int_gemm(xq_g, f["wq"]), xs_g, f["w_scale"], None, wl.out_dtype)
+                t4 = time.perf_counter()
+                acc["calibrate"][0] += t1 - t0
+                acc["calibrate"][1] += cal_s * k * esize + 4 * k
+                acc["fold"][0] += t2 - t1
+                acc["fold"][1] += 2 * n_s * k * esize + n_s * k + 4 * n_s + 16 * k
+                acc["norm_quant"][0] += t3 - t2
+                acc["norm_quant"][1] += m_s * k * esize + m_s * k + 4 * m_s + 4 * k * nparams
+                acc["gemm"][0] += t4 - t3
+                acc["gemm"][1] += 2.0 * gm_s * n_s * k
+            reps += 1
+            if time.perf_counter() - t_start >= budget_s or reps >= 50:
+                break
+    stages = {name: {"value": round(work / sec / (1e12 if name == "gemm" else 1e9), 6),
+                     "unit": "TOPS" if name == "gemm" else "GB/s", "seconds": round(sec, 3)}
+              for name, (sec, work) in acc.items()}
+    sample = (f"{reps} x every site at full K: calibration on {cal_s} tokens, fold of {n_s} weight rows, "
+              f"norm+quantise of {m_s} tokens, GEMM + epilogue of {gm_s} tokens x {n_s} output channels")
     model = None
     try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": ops / elapsed / 1e12, "unit": "TOPS", "cores": int(blas), "kind": "oracle", "sample": sample,
-            "seconds": elapsed, "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
-            "note": "numpy, single-threaded except the BLAS matrix product"}
+    return {"value": stages["gemm"]["value"], "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": sample, "stages": stages, "blas_threads": threads, "host_cpus": cores, "cpu_model": model,
+            "seconds": round(sum(sec for sec, _ in acc.values()), 3),
+            "note": "value is the GEMM stage; BLAS (the binary64 matrix product of the integer codes) runs on "
+                    "blas_threads threads, everything else single-threaded numpy"}
 
 
 def main():
@@ -1027,13 +1111,16 @@ def main():
         torch.cuda.synchronize()
     ms = (t1 - t0) * 1e3 / args.steps
     rep = kernel_report(timer, wl, sites)
-    gemm_ops = sum(2.0 * d["m"] * d["n"] * d["k"] for d in sites)
-    value = gemm_ops / (ms * 1e-3) / 1e12
-    g_ms = [rep[f"gemm{i}"]["ms"] for i in range(len(sites))]
-    g_ops = [2.0 * d["m"] * d["n"] * d["k"] for d in sites]
+    dims = [(d["m"], d["n"], d["k"]) for d in sites]
+    del sites
+    torch.cuda.empty_cache()
+    decode = None if args.no_decode else decode_block(torch, sq)
+    g_ops = [2.0 * dm * dn * dk for dm, dn, dk in dims]
+    value = sum(g_ops) / (ms * 1e-3) / 1e12
+    g_ms = [rep[f"gemm{i}"]["ms"] for i in range(len(dims))]
     achieved = sum(g_ops) / (sum(g_ms) * 1e-3) / 1e12
     osize = {"f32": 4, "f16": 2, "bf16": 2}[wl.out_dtype]
-    alg_bytes = [d["n"] * d["k"] + 4 * d["n"] + d["m"] * d["k"] + 4 * d["m"] + osize * d["m"] * d["n"] for d in sites]
+    alg_bytes = [dn * dk + 4 * dn + dm * dk + 4 * dm + osize * dm * dn for dm, dn, dk in dims]
     rec = recorded_traffic() if args.workload == 5 and m == 8192 else None
     traffic = rec["traffic_bytes_per_launch"] if rec else None
     sclk = rec.get("sclk_GHz") if rec else None
@@ -1058,6 +1145,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in rep.items()},
         "hbm_peak_GBps": PEAK_HBM_GBS,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

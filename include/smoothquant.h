@@ -24,8 +24,9 @@
  *    is reported as SQ_ERR_HIP. Faults during execution surface at the
  *    caller's next synchronisation. NaN and Inf inputs are outside the contract.
  *  - Shape limits: 1 <= M, N <= 2^31 - 1; 64 <= K <= SQ_K_MAX with K % 64 == 0
- *    (SQ_K_MAX keeps |acc| <= K * 127^2 inside int32). Matrix pointers must be
- *    16-byte aligned, vector pointers 4-byte aligned.
+ *    (SQ_K_MAX keeps |acc| <= K * 127^2 inside int32 for codes in [-127, 127],
+ *    the range every quantiser here produces). Matrix pointers must be 16-byte
+ *    aligned, vector pointers 4-byte aligned.
  *  - The library is re-entrant and thread-safe: it has no global state.
  *
  * Number format readings (the pages state none of them): an INT8 step is
@@ -138,6 +139,10 @@ sq_status sq_norm_quant(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
  * depth", section "Granularity: O1, O2, O3 ...": out = acc * scale_token[i] *
  * scale_channel[j], then conversion to FP16 or BF16).
  *   xq [M, K] int8, x_scale [M] fp32; wq [N, K] int8, w_scale [N] fp32.
+ *           The accumulator is exact for codes in [-127, 127] up to
+ *           K = SQ_K_MAX. The value -128 is multiplied exactly as well, but
+ *           with -128 codes present the int32 sum is guaranteed only up to
+ *           K = 131008 (K * 128^2 < 2^31); beyond that it may wrap.
  *   bias    [N] fp32 or NULL.
  *   y       [M, N] out, dtype y_dt:
  *           F32/F16/BF16: cvt(fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n]) (+ bias[n])),

@@ -86,7 +86,7 @@ import numpy as np
 __all__ = [
     "NONE", "LAYERNORM", "RMSNORM", "QMAX", "EPS_FOLD",
     "widen", "f32_to_bf16_bits", "round_output", "rn32_rational",
-    "row_stats", "normalize", "quantize_rows", "norm_quant", "norm_quant_row_variants",
+    "row_stats", "normalize", "quantize_rows", "norm_quant", "norm_quant_row_variants", "row_y_variants",
     "calibrate", "weight_colmax", "smoothing_factors", "fold",
     "int_gemm", "int_gemm_loops", "dequantize", "w8a8_linear",
     "quantize_tensor", "norm_quant_per_tensor", "static_step", "fold_per_tensor",
@@ -266,18 +266,25 @@ def norm_quant(x, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5):
     return q, step, info
 
 
-def norm_quant_row_variants(x_row, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5):
-    """Every (codes, step) a correct evaluation may give for one row whose statistics are near-ties."""
+def row_y_variants(x_row, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5):
+    """y of one row [1, K] for every correct rounding of its statistics (reading R2).
+
+    A statistic within NEAR_TIE of a binary32 rounding boundary may round to
+    either neighbour; every combination of the mean's and the variance's
+    admissible roundings gives one y. A row without a near-tie gives one y.
+    """
     x32 = widen(np.asarray(x_row)[None, :], dtype)
+    if norm == NONE:
+        return [normalize(x32, NONE, gamma=gamma_f)]
     st = row_stats(x32[0], norm)
     mus = {float(st["mu"])} | ({float(st["mu_other"])} if st["mu_dist"] < NEAR_TIE else set())
     vrs = {float(st["var"])} | ({float(st["var_other"])} if st["var_dist"] < NEAR_TIE else set())
-    out = []
-    for mu in sorted(mus):
-        for var in sorted(vrs):
-            y = normalize(x32, norm, [mu], [var], gamma_f, beta_f, eps)
-            out.append(quantize_rows(y))
-    return out
+    return [normalize(x32, norm, [mu], [var], gamma_f, beta_f, eps) for mu in sorted(mus) for var in sorted(vrs)]
+
+
+def norm_quant_row_variants(x_row, dtype, norm, gamma_f=None, beta_f=None, eps=1e-5):
+    """Every (codes, step) a correct evaluation may give for one row whose statistics are near-ties."""
+    return [quantize_rows(y) for y in row_y_variants(x_row, dtype, norm, gamma_f, beta_f, eps)]
 
 
 # --------------------------------------------------------------------------- O1 calibration

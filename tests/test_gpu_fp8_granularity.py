@@ -25,7 +25,8 @@ def test_norm_quant_fp8_per_tensor(dtype, norm, shape):
     xq, xs = sq.sq_norm_quant_fp8_per_tensor(_cuda(x), norm, _cuda(gamma), _cuda(beta), 1e-5)
     torch.cuda.synchronize()
     q, xsr, info = O.norm_quant_fp8_per_tensor(to_numpy(x), dtype, norm, _np(gamma), _np(beta), 1e-5)
-    _compare(q, xsr, info, host(xq), host(xs), f"{dtype}/{norm}/{m}x{k}")
+    _compare(q, xsr, info, host(xq), host(xs), f"{dtype}/{norm}/{m}x{k}",
+             (to_numpy(x), dtype, norm, _np(gamma), _np(beta), 1e-5), fp8=True)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
@@ -42,7 +43,8 @@ def test_norm_quant_fp8_static(dtype, norm, shape, factor):
     xq, xs = sq.sq_norm_quant_fp8_static(_cuda(x), st, norm, _cuda(gamma), _cuda(beta), 1e-5)
     torch.cuda.synchronize()
     q, xsr, info = O.norm_quant_fp8_per_tensor(to_numpy(x), dtype, norm, _np(gamma), _np(beta), 1e-5, step=step)
-    _compare(q, xsr, info, host(xq), host(xs), f"{dtype}/{norm}/{m}x{k}/x{factor}")
+    _compare(q, xsr, info, host(xq), host(xs), f"{dtype}/{norm}/{m}x{k}/x{factor}",
+             (to_numpy(x), dtype, norm, _np(gamma), _np(beta), 1e-5), fp8=True)
     codes = host(xq)
     assert not np.isin(codes, [0x7F, 0xFF]).any()                       # saturation, never NaN
     if factor < 1:
@@ -142,7 +144,8 @@ def test_fp8_static_pipeline_end_to_end():
     assert bits(np.array([step], F32)) == bits(host(st))
     q, xsr, info = O.norm_quant_fp8_per_tensor(to_numpy(x), "f16", "layernorm", f["gamma_f"], f["beta_f"], 1e-5,
                                                step=step)
-    _compare(q, xsr, info, host(xq), host(xs), "e2e8")
+    _compare(q, xsr, info, host(xq), host(xs), "e2e8",
+             (to_numpy(x), "f16", "layernorm", f["gamma_f"], f["beta_f"], 1e-5), fp8=True)
     mi, ni = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
     mi, ni = mi.ravel(), ni.ravel()
     acc, tol_acc = fp8_gemm_tolerance(host(xq), f["wq"], mi, ni)

@@ -128,7 +128,9 @@ def test_norm_quant_repeatable():
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("norm", ["none", "layernorm", "rmsnorm"])
-@pytest.mark.parametrize("shape", [(1, 64), (5, 4096), (64, 512), (513, 1024), (7, 20480)],
+@pytest.mark.parametrize("shape", [(1, 64), (5, 4096), (64, 512), (513, 1024), (7, 20480),
+                                   # the 1024-thread layouts of 6, 10, 13 and 17 vectors per thread
+                                   (5, 40960), (3, 81920), (2, 98304), (3, 133120)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_calibrate(dtype, norm, shape):
     m, k = shape
@@ -262,6 +264,22 @@ def test_gemm_int32_range_at_max_k():
         acc = host(sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)).astype(np.int64)
         assert np.array_equal(acc, O.int_gemm(xq.numpy(), wq.numpy()))
         assert acc.max() == k * 127 * 127
+
+
+def test_gemm_minus_128_codes_up_to_their_k_limit():
+    # -128 is a legal int8 operand although no quantiser here produces it: the products are exact, and
+    # the sum stays inside int32 while K * 128^2 < 2^31, i.e. up to K = 131008 (a multiple of 64)
+    k = 131008
+    assert k * 128 * 128 < 2 ** 31 <= (k + 64) * 128 * 128
+    for m, n in [(3, 5), (40, 300), (70, 5), (300, 520)]:     # decode and tiled kernels, K % 128 == 64
+        xq = torch.full((m, k), -128, dtype=torch.int8)
+        xq[1] = 127
+        wq = torch.full((n, k), -128, dtype=torch.int8)
+        wq[2] = 127
+        wq[3, ::2] = 0
+        acc = host(sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)).astype(np.int64)
+        assert np.array_equal(acc, O.int_gemm(xq.numpy(), wq.numpy())), f"{m}x{n}"
+        assert acc.max() == k * 128 * 128 and acc.min() == -k * 128 * 127
 
 
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])

@@ -56,13 +56,12 @@ def run_site(wl_id, site_idx, m, x_rows_cap=256, w_rows_cap=512):
     x_np = to_numpy(_gather(inp["x"], x_rows))
     ties = check_norm_quant(x_np, wl.dtype, norm, fref["gamma_f"], fref["beta_f"], EPS,
                             host(_gather(xq, x_rows)), host(_gather(xs, x_rows)), label="norm_quant")
-    xq_ref, xs_ref, _ = O.norm_quant(x_np, wl.dtype, norm, fref["gamma_f"], fref["beta_f"], EPS)
-    # outputs at the sampled (token, channel) pairs, from the oracle's own codes and steps
-    acc = O.int_gemm(xq_ref, fref["wq"])
-    out_ref, v32 = O.dequantize(acc, xs_ref, fref["w_scale"], None, wl.out_dtype)
-    if ties == 0:
-        y_sel = _gather(_gather(y, x_rows).t().contiguous(), w_rows).t().contiguous()
-        check_output(host(y_sel), out_ref, v32, wl.out_dtype, label="gemm")
+    # outputs at every sampled (token, channel) pair, from the codes and steps check_norm_quant has just
+    # accepted: the oracle's own, or on a near-tie row one of the row's correct roundings
+    acc = O.int_gemm(host(_gather(xq, x_rows)), fref["wq"])
+    out_ref, v32 = O.dequantize(acc, host(_gather(xs, x_rows)), fref["w_scale"], None, wl.out_dtype)
+    y_sel = _gather(_gather(y, x_rows).t().contiguous(), w_rows).t().contiguous()
+    check_output(host(y_sel), out_ref, v32, wl.out_dtype, label="gemm")
     print(f"  ok: {len(x_rows)} token rows, {len(w_rows)} weight rows checked; near-ties s={s_ties} rows={ties}",
           flush=True)
 
