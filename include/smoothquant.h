@@ -298,6 +298,57 @@ sq_status smoothquant_fold_fp8_per_tensor(const float* act_absmax, const void* w
                                           float* s_out, float* gamma_out, float* beta_out,
                                           uint8_t* wq, float* w_scale, void* stream);
 
+/*
+ * The LLM.int8() mixed-precision decomposition, the run-time alternative that
+ * SmoothQuant is set against ("LLM.int8() and SmoothQuant", section "Fix 1:
+ * give the outliers their own lane (LLM.int8())" and "going deeper / LLM.int8()
+ * decomposition"; "SmoothQuant, in depth", section "The problem SmoothQuant
+ * solves": a gather, a second GEMM and a merge at run time). Nothing is
+ * smoothed: the linear's input y is the norm output with the model's own
+ * gamma, beta (as smoothquant_calibrate records it), or x itself for
+ * SQ_NORM_NONE (gamma and beta are then ignored).
+ *   O        = {j : max_t |y[t, j]| >= tau} over this call's M tokens.
+ *   INT8 part: per token, step = fl32(max_{j not in O} |y[t, j]| / 127) and the
+ *            codes of those channels (code 0 on O); multiplied by wq, w_scale
+ *            (one step per output channel over all K, e.g. sq_norm_quant over
+ *            w with SQ_NORM_NONE and gamma_f NULL) and dequantised as
+ *            sq_w8a8_gemm does: deq = fl32(fl32(fl32(acc) * x_scale) * w_scale).
+ *   16-bit part: y[:, O] and w[:, O] rounded half to even to bf16 when w_dt is
+ *            BF16, else to fp16; acc16 = their product summed in binary32 on the
+ *            matrix cores (the summation order is the hardware's).
+ *   y        [M, N] = cvt(fl32(deq + acc16) (+ bias, one more binary32 add)).
+ *   x        [M, K] dtype x_dt; w [N, K] dtype w_dt (both F32, F16 or BF16).
+ *   tau      >= 0 (6 on the pages); +inf gives plain per-token W8A8, 0 the
+ *            16-bit product alone.
+ *   y_dt     F32, F16 or BF16; M <= 64 * 65535.
+ *   workspace  device memory of at least sq_llm_int8_workspace(M, N, K)->total
+ *            bytes, 256-byte aligned, owned by the caller; nothing in it needs
+ *            to be initialised. After the call has run it holds (offsets from
+ *            sq_llm_int8_workspace): count (int32: |O|), idx (int32 [K]: O
+ *            ascending, the first |O| valid), absmax (fp32 [K]: the call's
+ *            max_t |y[t, j]|), gamma_m / beta_m (fp32 [K]: gamma, beta with O
+ *            zeroed), stats (fp32 [M][2]: each token's mean and rstd, norms
+ *            only), xq (int8 [M, K]) and x_scale (fp32 [M]) of the INT8 part,
+ *            x16 ([M, P]) and w16 ([N, P]) the 16-bit operands as raw 16-bit
+ *            patterns, P = |O| rounded up to a multiple of 32 (zero padded),
+ *            and deq (fp32 [M, N]). Calls that share a workspace must be
+ *            ordered (one stream); the library keeps no pointer to it.
+ */
+typedef struct {
+  uint64_t total;
+  uint64_t count, idx, absmax, gamma_m, beta_m, stats, xq, x_scale, x16, w16, deq;
+} sq_llm_int8_layout;
+
+/* Workspace size and layout of sq_llm_int8_linear for these sizes (shape
+ * errors as sq_llm_int8_linear; no device work). */
+sq_status sq_llm_int8_workspace(int64_t M, int64_t N, int64_t K, sq_llm_int8_layout* layout);
+
+sq_status sq_llm_int8_linear(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                             sq_norm norm, const float* gamma, const float* beta, float eps, float tau,
+                             const void* w, sq_dtype w_dt, const int8_t* wq, const float* w_scale, int64_t N,
+                             const float* bias, void* y, sq_dtype y_dt,
+                             void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* sq_status_string(sq_status s);
 

@@ -44,7 +44,7 @@ from .smoothquant_oracle import (LAYERNORM, NONE, RMSNORM, dequantize, f32_to_bf
                                  quantize_rows, round_output, row_stats, widen)
 
 __all__ = ["TAU", "outlier_channels", "half_format", "round16", "weights", "activations", "gemm16",
-           "gemm16_bound", "decompose"]
+           "gemm16_bound", "decompose", "output_bound", "reference_output"]
 
 F32 = np.float32
 F64 = np.float64
@@ -118,17 +118,19 @@ def gemm16_bound(n_terms: int, sum_abs, k_step: int = 32) -> np.ndarray:
 
 
 def decompose(x, dtype, norm, w, gamma=None, beta=None, eps=1e-5, tau=TAU, w_dtype=None, wq=None, w_scale=None,
-              bias=None, out_dtype="f32"):
+              bias=None, out_dtype="f32", outliers=None):
     """The whole decomposition of one linear: Y = X_O W_O (16-bit) + dequantised INT8 product of the rest.
 
     x [M, K] in dtype, w [N, K] in w_dtype (default dtype); wq / w_scale default to weights(w).
+    `outliers` (ascending channel indices) replaces O found on these rows: to continue from the set
+    a whole batch gave when x holds only some of its rows.
     Returns a dict: y (the linear's input), near_tie, O, xq / x_scale (INT8 part, codes 0 on O),
     wq / w_scale, acc (int64), deq (binary32, before any bias), xo [M, |O|] and wo [N, |O|] (16-bit
     values), acc16 (binary64), sum_abs16 (sum of |products|), ref (binary64 deq + acc16 + bias).
     """
     w_dtype = w_dtype or dtype
     y, tie = activations(x, dtype, norm, gamma, beta, eps)
-    outl = outlier_channels(y, tau)
+    outl = outlier_channels(y, tau) if outliers is None else np.asarray(outliers, np.int64)
     y_int = y.copy()
     y_int[:, outl] = F32(0.0)
     xq, xs = quantize_rows(y_int)

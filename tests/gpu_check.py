@@ -115,3 +115,72 @@ def check_output(y_gpu_np, out_ref, v32_ref, out_dtype, label=""):
     assert np.all(np.abs(ref - v32_ref.astype(np.float64)) <= u * np.abs(v32_ref.astype(np.float64)) + half_ulp_min)
     exact = np.mean(bits(np.ascontiguousarray(y_gpu_np)) == bits(np.ascontiguousarray(out_ref)))
     assert exact == 1.0, f"{label}: {100 * (1 - exact):.4f}% of outputs not bit-identical"
+
+
+def _f16_bits(v32, fmt):
+    """Bit patterns of binary32 values that are fp16 / bf16 numbers."""
+    v32 = np.asarray(v32, F32)
+    return v32.astype(np.float16).view(np.uint16) if fmt == "f16" else O.f32_to_bf16_bits(v32)
+
+
+def check_llm_int8(x_np, dtype, norm, gamma, beta, eps, tau, w_np, w_dtype, out_dtype, parts, y_gpu, bias=None,
+                   outliers=None, label=""):
+    """The LLM.int8() decomposition on the GPU against oracle.llm_int8, part by part.
+
+    x_np holds the rows being checked (all of them, or a sample with `outliers` = the set the whole
+    batch gave); w_np all weight rows, or a sample of them (parts["deq"], parts["w16"] and y_gpu then
+    hold just those columns / rows). Integer and 16-bit parts are bit-exact: the outlier set (when x_np
+    is the whole batch), the INT8 codes and steps, the 16-bit operands, deq. A row whose statistics are a near-tie may take either rounding
+    (codes, step and 16-bit values of one of the oracle's candidate y rows). The output must lie within
+    output_bound of deq + the exact 16-bit product, both taken from the accepted parts.
+    """
+    import oracle.llm_int8 as L
+    count = parts["count"]
+    o_gpu = host(parts["idx"]).astype(np.int64)
+    assert len(o_gpu) == count and np.all(np.diff(o_gpu) > 0), f"{label}: outlier list not ascending"
+    d = L.decompose(x_np, dtype, norm, w_np, gamma, beta, eps, tau, w_dtype, bias=bias, out_dtype=out_dtype,
+                    outliers=o_gpu if outliers is None else outliers)
+    if outliers is None:
+        o_ref = L.outlier_channels(d["y"], tau)
+        if not np.array_equal(o_ref, o_gpu):
+            # only a near-tie row, normalised with its other statistic rounding, may move a channel across tau
+            assert d["near_tie"].any(), f"{label}: outliers {o_gpu[:8]} vs oracle {o_ref[:8]}"
+    else:
+        assert np.array_equal(np.asarray(outliers), o_gpu), f"{label}: outlier set differs"
+    o = d["O"]
+    fmt = d["fmt"]
+    p = (count + 31) // 32 * 32
+    xq_gpu, xs_gpu = host(parts["xq"]), host(parts["x_scale"])
+    x16_gpu = host(parts["x16"]).astype(F32)
+    assert x16_gpu.shape[1] == p and not x16_gpu[:, count:].any(), f"{label}: 16-bit padding not zero"
+    x16_bits = _f16_bits(x16_gpu[:, :count], fmt)
+    bad = np.where((xq_gpu != d["xq"]).any(axis=1) | (bits(xs_gpu) != bits(d["x_scale"]))
+                   | (x16_bits != _f16_bits(d["xo"], fmt)).any(axis=1))[0]
+    for r in bad:
+        assert d["near_tie"][r], f"{label}: row {r} differs (step {d['x_scale'][r]!r} vs {xs_gpu[r]!r})"
+        ok = False
+        for y in O.row_y_variants(x_np[r], dtype, norm, gamma, beta, eps):
+            yi = y.copy()
+            yi[:, o] = 0
+            q, s = O.quantize_rows(yi)
+            ok |= (np.array_equal(q[0], xq_gpu[r]) and bits(s)[0] == bits(xs_gpu[r:r + 1])[0]
+                   and np.array_equal(_f16_bits(L.round16(y[0, o], fmt), fmt), x16_bits[r]))
+        assert ok, f"{label}: near-tie row {r} matches no correct rounding"
+    w16_gpu = host(parts["w16"]).astype(F32)
+    assert w16_gpu.shape[1] == p and not w16_gpu[:, count:].any()
+    assert np.array_equal(_f16_bits(w16_gpu[:, :count], fmt), _f16_bits(d["wo"], fmt)), f"{label}: w16 differs"
+    _, deq = O.dequantize(O.int_gemm(xq_gpu, d["wq"]), xs_gpu, d["w_scale"])
+    deq_gpu = host(parts["deq"])
+    assert np.array_equal(bits(deq), bits(deq_gpu)), f"{label}: deq differs in {int((bits(deq) != bits(deq_gpu)).sum())}"
+    # the output, from the accepted parts
+    d2 = dict(d, deq=deq, xo=x16_gpu[:, :count])
+    d2["acc16"] = L.gemm16(d2["xo"], d["wo"])
+    d2["sum_abs16"] = L.gemm16(np.abs(d2["xo"]), np.abs(d["wo"]))
+    d2["ref"] = deq.astype(np.float64) + d2["acc16"] + (0.0 if bias is None else np.asarray(bias, np.float64)[None, :])
+    y = np.ascontiguousarray(np.asarray(y_gpu))
+    y64 = (y.astype(np.uint32) << 16).view(F32).astype(np.float64) if out_dtype == "bf16" else y.astype(np.float64)
+    err = np.abs(y64 - d2["ref"])
+    bound = L.output_bound(d2, n_pad=p)
+    worst = np.max(err / np.maximum(bound, 1e-300)) if err.size else 0.0
+    assert np.all(err <= bound), f"{label}: output outside the bound (worst {worst:.3g} of it)"
+    return d2, worst

@@ -25,7 +25,8 @@ def test_header_declares_the_calls():
                            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step",
                            "smoothquant_fold_per_tensor", "sq_norm_quant_fp8", "smoothquant_fold_fp8",
                            "sq_fp8_gemm", "sq_norm_quant_fp8_per_tensor", "sq_norm_quant_fp8_static",
-                           "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor", "sq_status_string"}
+                           "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor", "sq_llm_int8_workspace",
+                           "sq_llm_int8_linear", "sq_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -108,7 +109,39 @@ def fold8t(a=A, w=A, dt=1, n=16, k=512, alpha=0.5, eps=1e-5, norm=1, g=None, b=N
                                              wq, ws, None)
 
 
+WS = ctypes.c_void_p(1 << 24)         # a 256-byte aligned stand-in workspace (never dereferenced)
+WS_NEED = sq.sq_llm_int8_workspace(16, 64, 512)["total"]
+
+
+def llm(x=A, dt=1, m=16, k=512, norm=1, g=None, b=None, eps=1e-5, tau=6.0, w=A, wdt=1, wq=A, ws=A, n=64,
+        bias=None, y=A, ydt=1, work=WS, nbytes=WS_NEED):
+    return L.sq_llm_int8_linear(x, dt, m, k, norm, g, b, F(eps), F(tau), w, wdt, wq, ws, n, bias, y, ydt, work,
+                                nbytes, None)
+
+
+def test_llm_int8_workspace_layout():
+    lay = sq.sq_llm_int8_workspace(16, 64, 512)
+    offs = [lay[f] for f in sq._lib.LLM_INT8_FIELDS[1:]]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and lay["total"] % 256 == 0
+    # each region holds its worst case: |O| = K channels for the 16-bit operands
+    assert lay["x16"] - lay["x_scale"] >= 4 * 16 and lay["w16"] - lay["x16"] >= 2 * 16 * 512
+    assert lay["deq"] - lay["w16"] >= 2 * 64 * 512 and lay["total"] - lay["deq"] >= 4 * 16 * 64
+    lay2 = sq._lib._LlmLayout()
+    assert L.sq_llm_int8_workspace(0, 64, 512, ctypes.byref(lay2)) == 3
+    assert L.sq_llm_int8_workspace(16, 64, 100, ctypes.byref(lay2)) == 3
+    assert L.sq_llm_int8_workspace(16, 64, 512, None) == 1
+
+
 @pytest.mark.parametrize("call,code", [
+    (lambda: llm(x=None), 1), (lambda: llm(w=None), 1), (lambda: llm(wq=None), 1), (lambda: llm(ws=None), 1),
+    (lambda: llm(y=None), 1), (lambda: llm(work=None), 1),
+    (lambda: llm(dt=3), 2), (lambda: llm(wdt=3), 2), (lambda: llm(ydt=3), 2), (lambda: llm(ydt=9), 2),
+    (lambda: llm(m=0), 3), (lambda: llm(n=0), 3), (lambda: llm(k=100), 3), (lambda: llm(m=64 * 65535 + 1), 3),
+    (lambda: llm(nbytes=WS_NEED - 1), 3),
+    (lambda: llm(x=A4), 4), (lambda: llm(w=A4), 4), (lambda: llm(y=A4), 4),
+    (lambda: llm(work=ctypes.c_void_p((1 << 24) + 128)), 4),
+    (lambda: llm(tau=-1.0), 5), (lambda: llm(tau=float("nan")), 5), (lambda: llm(norm=7), 5),
+    (lambda: llm(norm=2, b=A), 5), (lambda: llm(norm=1, eps=0.0), 5),
     (lambda: nq8t(x=None), 1), (lambda: nq8t(xs=None), 1), (lambda: nq8t(dt=3), 2), (lambda: nq8t(k=100), 3),
     (lambda: nq8t(xq=A4), 4), (lambda: nq8t(norm=0, b=A), 5), (lambda: nq8t(norm=1, eps=0.0), 5),
     (lambda: nq8s(step=None), 1), (lambda: nq8s(x=None), 1), (lambda: nq8s(dt=7), 2), (lambda: nq8s(m=0), 3),

@@ -16,12 +16,15 @@ from ._lib import (  # noqa: F401
     SQ_NORM_RMSNORM,
     SmoothQuantError,
     lib,
+    llm_int8_parts,
     smoothquant_calibrate,
     smoothquant_fold,
     smoothquant_fold_fp8,
     smoothquant_fold_fp8_per_tensor,
     smoothquant_fold_per_tensor,
     sq_fp8_gemm,
+    sq_llm_int8_linear,
+    sq_llm_int8_workspace,
     sq_norm_quant,
     sq_norm_quant_fp8,
     sq_norm_quant_fp8_per_tensor,

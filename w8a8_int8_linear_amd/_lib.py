@@ -27,7 +27,15 @@ _NORM = {"none": SQ_NORM_NONE, "layernorm": SQ_NORM_LAYERNORM, "rmsnorm": SQ_NOR
 EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a8_gemm",
            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step", "smoothquant_fold_per_tensor",
            "sq_norm_quant_fp8", "smoothquant_fold_fp8", "sq_fp8_gemm", "sq_norm_quant_fp8_per_tensor",
-           "sq_norm_quant_fp8_static", "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor", "sq_status_string")
+           "sq_norm_quant_fp8_static", "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor",
+           "sq_llm_int8_workspace", "sq_llm_int8_linear", "sq_status_string")
+
+LLM_INT8_FIELDS = ("total", "count", "idx", "absmax", "gamma_m", "beta_m", "stats", "xq", "x_scale", "x16", "w16",
+                   "deq")
+
+
+class _LlmLayout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_uint64) for name in LLM_INT8_FIELDS]
 
 
 class SmoothQuantError(RuntimeError):
@@ -57,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sq_norm_quant_fp8_static.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P]
     lib.sq_static_step_fp8.argtypes = [P, P, I64, P, P]
     lib.smoothquant_fold_fp8_per_tensor.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
+    lib.sq_llm_int8_workspace.argtypes = [I64, I64, I64, ctypes.POINTER(_LlmLayout)]
+    lib.sq_llm_int8_linear.argtypes = [P, I, I64, I64, I, P, P, F, F, P, I, P, P, I64, P, P, I, P, ctypes.c_uint64, P]
     lib.sq_status_string.argtypes = [I]
     lib.sq_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -281,3 +291,62 @@ def sq_fp8_gemm(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.float16, y=
             _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), _ptr(y), _DT[y.dtype], m, n, k,
             _stream(xq)))
     return y
+
+
+def sq_llm_int8_workspace(m, n, k):
+    """Workspace layout of sq_llm_int8_linear for M x N x K: a dict of byte offsets and the total."""
+    lay = _LlmLayout()
+    _check("sq_llm_int8_workspace", lib.sq_llm_int8_workspace(int(m), int(n), int(k), ctypes.byref(lay)))
+    return {name: int(getattr(lay, name)) for name in LLM_INT8_FIELDS}
+
+
+def sq_llm_int8_linear(x, w, wq, w_scale, norm="none", gamma=None, beta=None, eps=1e-5, tau=6.0, bias=None,
+                       out_dtype=torch.float16, y=None, workspace=None):
+    """LLM.int8() decomposition: y [M, N] = 16-bit product of the channels whose |y| reaches tau + the
+    dequantised INT8 product of the rest. x [M, K], w [N, K] (the 16-bit weights), wq [N, K] int8 and
+    w_scale [N] (per-output-channel INT8 of w). Returns (y, workspace); the workspace (uint8, allocated
+    here when None) holds the parts listed by sq_llm_int8_workspace."""
+    _dev(x, "x", _ACT)
+    _dev(w, "w", _ACT)
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs w {tuple(w.shape)}")
+    _dev(wq, "wq", torch.int8, (n, k))
+    _dev(w_scale, "w_scale", torch.float32, (n,))
+    _dev(gamma, "gamma", torch.float32, (k,))
+    _dev(beta, "beta", torch.float32, (k,))
+    _dev(bias, "bias", torch.float32, (n,))
+    need = sq_llm_int8_workspace(m, n, k)["total"]
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    if y is None:
+        y = torch.empty(m, n, dtype=out_dtype, device=x.device)
+    _dev(y, "y", out_dtype, (m, n))
+    with torch.cuda.device(x.device):
+        _check("sq_llm_int8_linear", lib.sq_llm_int8_linear(
+            _ptr(x), _DT[x.dtype], m, k, _NORM[norm], _ptr(gamma), _ptr(beta), eps, float(tau), _ptr(w), _DT[w.dtype],
+            _ptr(wq), _ptr(w_scale), n, _ptr(bias), _ptr(y), _DT[y.dtype], _ptr(workspace), workspace.numel(),
+            _stream(x)))
+    return y, workspace
+
+
+def llm_int8_parts(workspace, m, n, k, w_dtype=torch.float16):
+    """Views of the parts an sq_llm_int8_linear call left in its workspace (after synchronisation):
+    count, idx, absmax, gamma_m, beta_m, stats [M, 2], xq [M, K], x_scale [M], x16 [M, P] and w16 [N, P]
+    (16-bit values, P = |O| padded to 32), deq [M, N]."""
+    lay = sq_llm_int8_workspace(m, n, k)
+    half = torch.bfloat16 if w_dtype == torch.bfloat16 else torch.float16
+
+    def view(name, dtype, count):
+        nbytes = count * torch.empty(0, dtype=dtype).element_size()
+        return workspace[lay[name]:lay[name] + nbytes].view(dtype)
+    count = int(view("count", torch.int32, 1).item())
+    p = (count + 31) // 32 * 32
+    return {"count": count, "idx": view("idx", torch.int32, k)[:count],
+            "absmax": view("absmax", torch.float32, k), "gamma_m": view("gamma_m", torch.float32, k),
+            "beta_m": view("beta_m", torch.float32, k), "stats": view("stats", torch.float32, 2 * m).view(m, 2),
+            "xq": view("xq", torch.int8, m * k).view(m, k), "x_scale": view("x_scale", torch.float32, m),
+            "x16": view("x16", half, m * p).view(m, p), "w16": view("w16", half, n * p).view(n, p),
+            "deq": view("deq", torch.float32, m * n).view(m, n)}

@@ -47,11 +47,12 @@ static __constant__ float kZeros8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f
 // (x * rstd) * gamma; a NULL gamma / beta means 1 / 0. Sums are taken in
 // binary64 in a fixed order and rounded once to binary32 (LayerNorm: the
 // variance in one pass where that is provably accurate enough, else centred on
-// the binary64 mean); rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))).
+// the binary64 mean); rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))). With st
+// non-NULL, thread 0 also writes (mean, rstd) there (mean 0 for RMSNorm).
 template <int NORM, int NV, int THREADS>
 __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const float* __restrict__ gamma,
                                               const float* __restrict__ beta, float eps, RedRing<THREADS>& red,
-                                              int& rk) {
+                                              int& rk, float* __restrict__ st = nullptr) {
   const int nvec = K >> 3;
   float mu = 0.0f, r = 1.0f;
   if constexpr (NORM == SQ_NORM_LAYERNORM) {
@@ -128,6 +129,10 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
     for (int i = 0; i < NV; ++i) s2 += p2[i];
     s2 = block_sum<THREADS>(s2, red.at(rk++));
     r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
+  }
+  if (st != nullptr && threadIdx.x == 0) {
+    st[0] = mu;
+    st[1] = r;
   }
   const float* gp = gamma ? gamma : kOnes8;
   const float* bp = beta ? beta : kZeros8;
@@ -234,14 +239,16 @@ __device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
 //        before the reduction; wide rows recompute the product in pass two
 //        and refill vector i right after its codes are written.
 //  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
-//        normalise in place, then max and codes.
-template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS, bool FP8 = false>
+//        normalise in place, then max and codes; STATS also writes the
+//        row's (mean, rstd) to stats[2 row], stats[2 row + 1].
+template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS, bool FP8 = false, bool STATS = false>
 __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
                                              int64_t row, int64_t next, int M, int K,
                                              const float* __restrict__ gamma,
                                              const ColVec<NV, THREADS, GREG, GLDS>& gv,
                                              const float* __restrict__ beta, float eps, int8_t* __restrict__ xq,
-                                             float* __restrict__ x_scale, RedRing<THREADS>& red, int& rk) {
+                                             float* __restrict__ x_scale, RedRing<THREADS>& red, int& rk,
+                                             float* __restrict__ stats = nullptr) {
   const int nvec = K >> 3;
   constexpr int B = Storage<T>::kBytes;
   int8_t* qrow = xq + row * K;
@@ -320,7 +327,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
         if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
       }
     }
-    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
+    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk, STATS ? stats + 2 * row : nullptr);
     float pm[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -349,6 +356,7 @@ constexpr int kRowsAmax = 1;         // per-tensor first pass: each row's max |y
 constexpr int kRowsGivenStep = 2;    // per-tensor codes with a step given for the whole tensor, clipped
 constexpr int kRowsFp8 = 3;          // one step per row, FP8 (OCP E4M3) codes: step = absmax / 448
 constexpr int kRowsFp8GivenStep = 4; // FP8 codes with a step given for the whole tensor, saturated to +-448
+constexpr int kRowsStats = 5;        // as kRowsPerRow, and each row's (mean, rstd) written out (norms only)
 
 // One row of a per-tensor pass: MODE kRowsAmax writes the row's max |y| alone
 // (the first pass of a per-tensor dynamic step); kRowsGivenStep writes the
@@ -465,7 +473,8 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, float eps,
                                                         int8_t* __restrict__ xq, float* __restrict__ x_scale,
-                                                        const float* __restrict__ step_ptr, int write_scale) {
+                                                        const float* __restrict__ step_ptr, int write_scale,
+                                                        float* __restrict__ stats) {
   __shared__ RedRing<THREADS> red;
   // NONE keeps its column factors for the workgroup's lifetime (the norms read
   // gamma / beta once per row)
@@ -489,8 +498,8 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
                                                        red, rk, qz, write_scale != 0);
   } else {
     for (int64_t row = blockIdx.x; row < M; row += G)
-      quantize_row<T, NORM, NV, THREADS, kReg, kLds, MODE == kRowsFp8>(raw, x, row, row + G, M, K, gamma, gv, beta,
-                                                                       eps, xq, x_scale, red, rk);
+      quantize_row<T, NORM, NV, THREADS, kReg, kLds, MODE == kRowsFp8, MODE == kRowsStats>(
+          raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk, stats);
   }
 }
 
@@ -550,7 +559,7 @@ hipError_t launch_nq(const RowArgs& a, const float* step_ptr, int write_scale, h
   if (hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), THREADS, &cap)) return e;
   const int grid = static_cast<int>(a.rows < cap ? a.rows : cap);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, st, a.x, static_cast<int>(a.rows), a.K, a.gamma, a.beta,
-                     a.eps, a.xq, a.x_scale, step_ptr, write_scale);
+                     a.eps, a.xq, a.x_scale, step_ptr, write_scale, a.stats);
   return hipGetLastError();
 }
 

@@ -14,6 +14,37 @@ sq_status from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; 
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Workspace regions of the LLM.int8() decomposition, each 256-byte aligned, in
+// this order. The 16-bit operands are sized for every channel an outlier.
+sq_llm_int8_layout llm_layout(int64_t M, int64_t N, int64_t K) {
+  sq_llm_int8_layout l{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = (off + bytes + 255) & ~uint64_t{255};
+    return at;
+  };
+  const uint64_t m = static_cast<uint64_t>(M), n = static_cast<uint64_t>(N), k = static_cast<uint64_t>(K);
+  l.count = take(4);
+  l.idx = take(4 * k);
+  l.absmax = take(4 * k);
+  l.gamma_m = take(4 * k);
+  l.beta_m = take(4 * k);
+  l.stats = take(8 * m);
+  l.xq = take(m * k);
+  l.x_scale = take(4 * m);
+  l.x16 = take(2 * m * k);
+  l.w16 = take(2 * n * k);
+  l.deq = take(4 * m * n);
+  l.total = off;
+  return l;
+}
+
+template <typename T>
+T* at(void* base, uint64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +198,32 @@ sq_status smoothquant_fold_fp8_per_tensor(const float* act_absmax, const void* w
   if (sq_status s = from_hip(sq::launch_fold_colmax_scales(f, st))) return s;
   sq::RowArgs r{w, w_dt, N, static_cast<int>(K), SQ_NORM_NONE, s_out, nullptr, 1.0f, q, w_scale, nullptr};
   return from_hip(sq::launch_norm_quant_fp8_per_tensor(r, st));
+}
+
+sq_status sq_llm_int8_workspace(int64_t M, int64_t N, int64_t K, sq_llm_int8_layout* layout) {
+  if (!layout) return SQ_ERR_NULL_POINTER;
+  if (M < 1 || M > sq::kLlmMaxTokens || N < 1 || N > 2147483647LL || K < 64 || K > SQ_K_MAX || K % 64 != 0)
+    return SQ_ERR_BAD_SHAPE;
+  *layout = llm_layout(M, N, K);
+  return SQ_OK;
+}
+
+sq_status sq_llm_int8_linear(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm, const float* gamma,
+                             const float* beta, float eps, float tau, const void* w, sq_dtype w_dt,
+                             const int8_t* wq, const float* w_scale, int64_t N, const float* bias, void* y,
+                             sq_dtype y_dt, void* workspace, uint64_t workspace_bytes, void* stream) {
+  const bool shape_ok = M >= 1 && M <= sq::kLlmMaxTokens && N >= 1 && K >= 64 && K <= SQ_K_MAX && K % 64 == 0;
+  const uint64_t need = shape_ok ? llm_layout(M, N, K).total : 0;
+  if (sq_status s = sq::check_llm_int8(x, x_dt, M, K, norm, gamma, beta, eps, tau, w, w_dt, wq, w_scale, N, bias, y,
+                                       y_dt, workspace, workspace_bytes, need))
+    return s;
+  const sq_llm_int8_layout l = llm_layout(M, N, K);
+  sq::LlmArgs a{x, x_dt, M, static_cast<int>(K), norm, gamma, beta, eps, tau, w, w_dt, wq, w_scale, N, bias, y, y_dt,
+                at<float>(workspace, l.absmax), at<int>(workspace, l.count), at<int>(workspace, l.idx),
+                at<float>(workspace, l.gamma_m), at<float>(workspace, l.beta_m), at<float>(workspace, l.stats),
+                at<int8_t>(workspace, l.xq), at<float>(workspace, l.x_scale), at<uint16_t>(workspace, l.x16),
+                at<uint16_t>(workspace, l.w16), at<float>(workspace, l.deq)};
+  return from_hip(sq::launch_llm_int8(a, as_stream(stream)));
 }
 
 const char* sq_status_string(sq_status s) {

@@ -21,6 +21,7 @@ struct RowArgs {
   int8_t* xq;
   float* x_scale;
   float* absmax;
+  float* stats = nullptr;   // (mean, rstd) per row, written by the norm-statistics launch only
 };
 
 struct FoldArgs {
@@ -48,7 +49,41 @@ struct GemmArgs {
   int M, N, K;
 };
 
+// The LLM.int8() decomposition: inputs, output, and the workspace regions it uses.
+struct LlmArgs {
+  const void* x;
+  sq_dtype x_dt;
+  int64_t M;
+  int K;
+  sq_norm norm;
+  const float* gamma;
+  const float* beta;
+  float eps;
+  float tau;
+  const void* w;
+  sq_dtype w_dt;
+  const int8_t* wq;
+  const float* w_scale;
+  int64_t N;
+  const float* bias;
+  void* y;
+  sq_dtype y_dt;
+  // workspace
+  float* absmax;      // [K]
+  int* count;         // [1]
+  int* idx;           // [K]
+  float* gamma_m;     // [K]
+  float* beta_m;      // [K]
+  float* stats;       // [2 M]
+  int8_t* xq;         // [M, K]
+  float* x_scale;     // [M]
+  uint16_t* x16;      // [M, K] at most
+  uint16_t* w16;      // [N, K] at most
+  float* deq;         // [M, N]
+};
+
 hipError_t launch_norm_quant(const RowArgs& a, hipStream_t st);
+hipError_t launch_llm_int8(const LlmArgs& l, hipStream_t st);
 hipError_t launch_calibrate(const RowArgs& a, hipStream_t st);
 // Column maxima of W into s_out, then s, gamma', beta' (the weight codes are a
 // norm_quant pass over W with gamma = s).

@@ -99,4 +99,28 @@ sq_status check_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, c
   return SQ_OK;
 }
 
+sq_status check_llm_int8(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm, const float* gamma,
+                         const float* beta, float eps, float tau, const void* w, sq_dtype w_dt, const int8_t* wq,
+                         const float* w_scale, int64_t N, const float* bias, const void* y, sq_dtype y_dt,
+                         const void* workspace, uint64_t workspace_bytes, uint64_t workspace_needed) {
+  if (!x || !w || !wq || !w_scale || !y || !workspace) return SQ_ERR_NULL_POINTER;
+  if (!input_dtype(x_dt) || !input_dtype(w_dt)) return SQ_ERR_BAD_DTYPE;
+  if (y_dt != SQ_DT_F32 && y_dt != SQ_DT_F16 && y_dt != SQ_DT_BF16) return SQ_ERR_BAD_DTYPE;
+  if (sq_status s = check_rows(M)) return s;
+  if (M > kLlmMaxTokens) return SQ_ERR_BAD_SHAPE;
+  if (sq_status s = check_rows(N)) return s;
+  if (sq_status s = check_k(K)) return s;
+  if (!norm_known(norm)) return SQ_ERR_BAD_ARG;
+  if (norm != SQ_NORM_NONE) {
+    if (sq_status s = check_norm_params(norm, gamma, beta)) return s;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return SQ_ERR_BAD_ARG;
+  }
+  if (!(tau >= 0.0f)) return SQ_ERR_BAD_ARG;                 // NaN or negative; +inf means no outlier
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(wq, 16) || !aligned(y, 16)) return SQ_ERR_MISALIGNED;
+  if (!aligned(w_scale, 4) || !aligned(bias, 4)) return SQ_ERR_MISALIGNED;
+  if (!aligned(workspace, 256)) return SQ_ERR_MISALIGNED;
+  if (workspace_bytes < workspace_needed) return SQ_ERR_BAD_SHAPE;
+  return SQ_OK;
+}
+
 }  // namespace sq

@@ -27,4 +27,12 @@ sq_status check_static_step(const float* act_absmax, const float* s, int64_t K, 
 sq_status check_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
                      const float* bias, const void* y, sq_dtype y_dt, int64_t M, int64_t N, int64_t K);
 
+// The LLM.int8() decomposition: every input as above, tau >= 0 (not NaN), the
+// workspace 256-byte aligned and at least workspace_needed bytes.
+constexpr int64_t kLlmMaxTokens = 64LL * 65535;            // the merge grid's token blocks
+sq_status check_llm_int8(const void* x, sq_dtype x_dt, int64_t M, int64_t K, sq_norm norm, const float* gamma,
+                         const float* beta, float eps, float tau, const void* w, sq_dtype w_dt, const int8_t* wq,
+                         const float* w_scale, int64_t N, const float* bias, const void* y, sq_dtype y_dt,
+                         const void* workspace, uint64_t workspace_bytes, uint64_t workspace_needed);
+
 }  // namespace sq
