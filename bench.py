@@ -63,6 +63,11 @@ def parse():
                         "exit; with --decode-sweep / --summarize-decode, the FP8 decode GEMMs instead")
     p.add_argument("--summarize-fp8", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats of --fp8 into a profiles/ table and exit")
+    p.add_argument("--llm-int8", action="store_true",
+                   help="time LLM.int8()'s decomposition beside the SmoothQuant run-time path on the OPT-6.7B and "
+                        "MT-NLG-530B-width sites, and exit")
+    p.add_argument("--summarize-llm-int8", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace --stats of --llm-int8 into a profiles/ table and exit")
     p.add_argument("--prefill-sweep", action="store_true",
                    help="time the prefill GEMMs of every workload (fp16 out) and exit")
     p.add_argument("--summarize-decode-counters", metavar="PMC_DIR",
@@ -734,6 +739,69 @@ def fp8_sweep(args):
         torch.cuda.empty_cache()
 
 
+# ----------------------------------------------------------------------------- LLM.int8() against SmoothQuant
+
+LLM_TAU = 6.0          # the outlier threshold on the LLM.int8() page ("going deeper", tau = 6)
+LLM_CMD = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
+           "python3 bench.py --llm-int8")
+
+
+def llm_int8_sweep(args):
+    """The run-time path of SmoothQuant (fused norm + per-token INT8 quantiser, then the INT8 GEMM with
+    its epilogue, on the folded parameters) beside LLM.int8()'s decomposition of the same linear (its
+    whole run-time call: per-channel maxima of the batch, outlier selection, quantiser, 16-bit gather,
+    INT8 GEMM into binary32, 16-bit product and merge), on every site of the OPT-6.7B and MT-NLG-530B-
+    width workloads. Offline work (calibration and fold; LLM.int8()'s weight quantisation) is done first
+    and not timed. HIP-event medians of whole calls (MT-NLG: 5 launches, OPT: 20)."""
+    import torch
+    import w8a8_int8_linear_amd as sq
+    from synth import WORKLOADS
+    for wl_id in (2, 5):
+        wl = WORKLOADS[wl_id]
+        sites = build_sites(torch, sq, wl, wl.m[0])
+        reps = 5 if wl_id == 5 else 20
+        for d in sites:
+            m, k, n, norm = d["m"], d["k"], d["n"], d["norm"]
+            amax = sq.smoothquant_calibrate(d["x_cal"], norm, d["gamma"], d["beta"], EPS)
+            fo = sq.smoothquant_fold(amax, d["w"], wl.alpha, EPS, norm, d["gamma"], d["beta"], out=d["fold"])
+            wq, ws = sq.sq_norm_quant(d["w"], "none")
+            work = torch.empty(sq.sq_llm_int8_workspace(m, n, k)["total"], dtype=torch.uint8, device="cuda")
+            y2 = torch.empty_like(d["y"])
+
+            def smoothquant():
+                sq.sq_norm_quant(d["x"], norm, fo["gamma_f"], fo["beta_f"], EPS, d["xq"], d["xs"])
+                sq.sq_w8a8_gemm(d["xq"], d["xs"], fo["wq"], fo["w_scale"], y=d["y"], out_dtype=d["y"].dtype)
+
+            def llm_int8():
+                sq.sq_llm_int8_linear(d["x"], d["w"], wq, ws, norm, d["gamma"], d["beta"], EPS, LLM_TAU,
+                                      out_dtype=y2.dtype, y=y2, workspace=work)
+            t_sq = median_ms(torch, smoothquant, reps)
+            t_li = median_ms(torch, llm_int8, reps)
+            count = sq.llm_int8_parts(work, m, n, k, d["w"].dtype)["count"]
+            print(json.dumps({"workload": wl.name, "site": d["site"].name, "mnk": [m, n, k],
+                              "outlier_channels": count, "smoothquant_ms": round(t_sq, 4),
+                              "llm_int8_ms": round(t_li, 4), "llm_int8_over_smoothquant": round(t_li / t_sq, 3)}),
+                  flush=True)
+            del work, y2, wq, ws
+            torch.cuda.empty_cache()
+        del sites
+        torch.cuda.empty_cache()
+
+
+def summarize_llm_int8(trace_dir):
+    """Kernel statistics of a --llm-int8 run as a profiles/ table."""
+    kernel_stats_table(
+        trace_dir, "LLM.int8() decomposition beside the SmoothQuant run-time path, OPT-6.7B and MT-NLG-530B-width "
+        "sites", LLM_CMD, "--summarize-llm-int8",
+        "Per site, 20 (OPT-6.7B) or 5 (MT-NLG) timed calls plus one warm-up of each path, after the untimed "
+        "offline work. SmoothQuant at run time: `k_norm_quant` (mode 0) then the INT8 GEMM. LLM.int8(): "
+        "`k_fill_zero_f32` + the per-channel maxima (`k_calibrate` / `k_colmax`), `k_outlier_select`, "
+        "`k_norm_quant` (mode 5 with a norm: also the row statistics; mode 0 without), `k_outlier_gather`, "
+        "the INT8 GEMM into binary32, `k_outlier_merge`. The offline kernels (calibration, fold, weight "
+        "quantisation) appear too; each kernel's row mixes every site it ran on.",
+        "llm_int8_vs_smoothquant.md")
+
+
 def summarize_fp8(trace_dir):
     """Per-dispatch durations of a --fp8 kernel trace, grouped by kernel and grid (one kernel name
     serves both the activation quantiser and the fold's weight quantiser), as a profiles/ table."""
@@ -1063,6 +1131,9 @@ def main():
     if args.summarize_prefill:
         summarize_prefill(args.summarize_prefill)
         return
+    if args.summarize_llm_int8:
+        summarize_llm_int8(args.summarize_llm_int8)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",
                           "n_gpus": args.gpus}))
@@ -1072,6 +1143,9 @@ def main():
         return
     if args.prefill_sweep:
         prefill_sweep()
+        return
+    if args.llm_int8:
+        llm_int8_sweep(args)
         return
     if args.granularities:
         granularity_sweep(args)

@@ -117,6 +117,12 @@ def check_output(y_gpu_np, out_ref, v32_ref, out_dtype, label=""):
     assert exact == 1.0, f"{label}: {100 * (1 - exact):.4f}% of outputs not bit-identical"
 
 
+def _vals16(t, fmt):
+    """A device tensor of fp16 / bf16 numbers as binary32 values (host() gives bf16 as bit patterns)."""
+    a = host(t)
+    return O.widen(a, "bf16") if fmt == "bf16" else a.astype(F32)
+
+
 def _f16_bits(v32, fmt):
     """Bit patterns of binary32 values that are fp16 / bf16 numbers."""
     v32 = np.asarray(v32, F32)
@@ -151,7 +157,7 @@ def check_llm_int8(x_np, dtype, norm, gamma, beta, eps, tau, w_np, w_dtype, out_
     fmt = d["fmt"]
     p = (count + 31) // 32 * 32
     xq_gpu, xs_gpu = host(parts["xq"]), host(parts["x_scale"])
-    x16_gpu = host(parts["x16"]).astype(F32)
+    x16_gpu = _vals16(parts["x16"], fmt)
     assert x16_gpu.shape[1] == p and not x16_gpu[:, count:].any(), f"{label}: 16-bit padding not zero"
     x16_bits = _f16_bits(x16_gpu[:, :count], fmt)
     bad = np.where((xq_gpu != d["xq"]).any(axis=1) | (bits(xs_gpu) != bits(d["x_scale"]))
@@ -166,7 +172,7 @@ def check_llm_int8(x_np, dtype, norm, gamma, beta, eps, tau, w_np, w_dtype, out_
             ok |= (np.array_equal(q[0], xq_gpu[r]) and bits(s)[0] == bits(xs_gpu[r:r + 1])[0]
                    and np.array_equal(_f16_bits(L.round16(y[0, o], fmt), fmt), x16_bits[r]))
         assert ok, f"{label}: near-tie row {r} matches no correct rounding"
-    w16_gpu = host(parts["w16"]).astype(F32)
+    w16_gpu = _vals16(parts["w16"], fmt)
     assert w16_gpu.shape[1] == p and not w16_gpu[:, count:].any()
     assert np.array_equal(_f16_bits(w16_gpu[:, :count], fmt), _f16_bits(d["wo"], fmt)), f"{label}: w16 differs"
     _, deq = O.dequantize(O.int_gemm(xq_gpu, d["wq"]), xs_gpu, d["w_scale"])
