@@ -66,8 +66,9 @@ def parse():
     p.add_argument("--llm-int8", action="store_true",
                    help="time LLM.int8()'s decomposition beside the SmoothQuant run-time path on the OPT-6.7B and "
                         "MT-NLG-530B-width sites, and exit")
-    p.add_argument("--summarize-llm-int8", metavar="TRACE_DIR",
-                   help="turn a rocprofv3 --kernel-trace --stats of --llm-int8 into a profiles/ table and exit")
+    p.add_argument("--summarize-llm-int8", nargs="+", metavar="PATH",
+                   help="TRACE_DIR [SWEEP_STDOUT]: turn a rocprofv3 --kernel-trace --stats of --llm-int8 (and the "
+                        "run's stdout) into a profiles/ table and exit")
     p.add_argument("--prefill-sweep", action="store_true",
                    help="time the prefill GEMMs of every workload (fp16 out) and exit")
     p.add_argument("--summarize-decode-counters", metavar="PMC_DIR",
@@ -788,8 +789,9 @@ def llm_int8_sweep(args):
         torch.cuda.empty_cache()
 
 
-def summarize_llm_int8(trace_dir):
-    """Kernel statistics of a --llm-int8 run as a profiles/ table."""
+def summarize_llm_int8(trace_dir, sweep_log=None):
+    """Kernel statistics of a --llm-int8 run as a profiles/ table; with the run's stdout (sweep_log),
+    also its per-site HIP-event medians."""
     kernel_stats_table(
         trace_dir, "LLM.int8() decomposition beside the SmoothQuant run-time path, OPT-6.7B and MT-NLG-530B-width "
         "sites", LLM_CMD, "--summarize-llm-int8",
@@ -800,6 +802,18 @@ def summarize_llm_int8(trace_dir):
         "the INT8 GEMM into binary32, `k_outlier_merge`. The offline kernels (calibration, fold, weight "
         "quantisation) appear too; each kernel's row mixes every site it ran on.",
         "llm_int8_vs_smoothquant.md")
+    if sweep_log:
+        recs = [json.loads(ln) for ln in open(sweep_log) if ln.startswith("{")]
+        lines = ["", "Per site, HIP-event medians of whole calls in the same run (the profiler's overhead included):",
+                 "", "| workload | site | M x N x K | outlier channels | SmoothQuant ms | LLM.int8() ms | ratio |",
+                 "|---|---|---|---|---|---|---|"]
+        for r in recs:
+            m, n, k = r["mnk"]
+            lines.append(f"| {r['workload']} | {r['site']} | {m} x {n} x {k} | {r['outlier_channels']} | "
+                         f"{r['smoothquant_ms']:.4f} | {r['llm_int8_ms']:.4f} | {r['llm_int8_over_smoothquant']:.2f} |")
+        with open(os.path.join(ROOT, "profiles", "llm_int8_vs_smoothquant.md"), "a") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
 
 
 def summarize_fp8(trace_dir):
@@ -1132,7 +1146,7 @@ def main():
         summarize_prefill(args.summarize_prefill)
         return
     if args.summarize_llm_int8:
-        summarize_llm_int8(args.summarize_llm_int8)
+        summarize_llm_int8(*args.summarize_llm_int8[:2])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not part of it",

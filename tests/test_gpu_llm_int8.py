@@ -200,14 +200,16 @@ def test_llm_int8_workload_site(wl_id, site_idx, m):
     # the outlier set, against a binary64 evaluation of every row (channels near tau are left open)
     a64 = _approx_outliers(inp["x"], site.norm, gamma, beta, L.TAU)
     a_gpu = host(parts["absmax"]).astype(np.float64)
-    assert np.all(np.abs(a_gpu - a64) <= 1e-5 * a64 + 1e-30), f"{label}: absmax"
+    # relative near tau and above; absolute below 1, where a single token's y can cancel to ~0
+    assert np.all(np.abs(a_gpu - a64) <= 1e-5 * np.maximum(a64, 1.0)), f"{label}: absmax"
     o_gpu = host(parts["idx"]).astype(np.int64)
     assert np.array_equal(o_gpu, np.where(a_gpu >= L.TAU)[0])
     sure = np.abs(a64 - L.TAU) > 1e-4 * L.TAU
     member = np.zeros(site.k, bool)
     member[o_gpu] = True
     assert np.array_equal(member[sure], (a64 >= L.TAU)[sure]), f"{label}: outlier set"
-    assert set(inp["outliers"].tolist()) <= set(o_gpu.tolist()), f"{label}: a planted outlier channel is missing"
+    if m >= 64:            # with a few tokens a planted channel's own draws may all stay below tau
+        assert set(inp["outliers"].tolist()) <= set(o_gpu.tolist()), f"{label}: a planted outlier channel is missing"
     _check_masks(parts, inp["gamma"], inp["beta"], site.k, label)
     # sampled token rows x sampled weight rows, bit for bit against the oracle with the batch's set
     rows = _sample(m, 24, 1)
