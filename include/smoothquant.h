@@ -27,7 +27,9 @@
  *    (SQ_K_MAX keeps |acc| <= K * 127^2 inside int32 for codes in [-127, 127],
  *    the range every quantiser here produces). Matrix pointers must be 16-byte
  *    aligned, vector pointers 4-byte aligned.
- *  - The library is re-entrant and thread-safe: it has no global state.
+ *  - The library is re-entrant and thread-safe: its only global state is the
+ *    per-device address of the fixed scratch of sq_llm_int8_linear_noalloc,
+ *    looked up once under a lock.
  *
  * Number format readings (the pages state none of them): an INT8 step is
  * fl32(absmax / 127) with IEEE division, codes are round-half-to-even of
@@ -47,6 +49,9 @@ extern "C" {
 
 #define SQ_K_MAX 133120
 
+/* Device scratch that sq_llm_int8_linear_noalloc uses in place of a workspace. */
+#define SQ_NOALLOC_SCRATCH_BYTES ((uint64_t)134217728)
+
 typedef enum {
   SQ_OK = 0,
   SQ_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
@@ -55,7 +60,8 @@ typedef enum {
   SQ_ERR_MISALIGNED = 4,    /* pointer alignment below the stated minimum */
   SQ_ERR_BAD_ARG = 5,       /* alpha outside [0, 1], eps <= 0, unknown norm, illegal combination */
   SQ_ERR_UNSUPPORTED = 6,   /* valid request this build does not implement */
-  SQ_ERR_HIP = 7            /* the HIP runtime refused a launch */
+  SQ_ERR_HIP = 7,           /* the HIP runtime refused a launch */
+  SQ_ERR_TOO_LARGE = 8      /* the call needs more than SQ_NOALLOC_SCRATCH_BYTES of scratch */
 } sq_status;
 
 typedef enum { SQ_DT_F32 = 0, SQ_DT_F16 = 1, SQ_DT_BF16 = 2, SQ_DT_I32 = 3 } sq_dtype;
@@ -348,6 +354,24 @@ sq_status sq_llm_int8_linear(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
                              const void* w, sq_dtype w_dt, const int8_t* wq, const float* w_scale, int64_t N,
                              const float* bias, void* y, sq_dtype y_dt,
                              void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * sq_llm_int8_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, results and errors as
+ * sq_llm_int8_linear. The workspace is a fixed array of
+ * SQ_NOALLOC_SCRATCH_BYTES inside the library: each GPU it runs on holds one
+ * copy until the process ends. A call whose sq_llm_int8_workspace(M, N, K)
+ * total exceeds that returns SQ_ERR_TOO_LARGE and enqueues nothing. The call
+ * itself allocates nothing (its first call on a device only looks up the
+ * array's address there). Every call on one GPU shares that GPU's array and
+ * leaves the last call's parts in it, so calls that overlap on one GPU (other
+ * streams, other threads) race; calls ordered on one stream do not.
+ */
+sq_status sq_llm_int8_linear_noalloc(const void* x, sq_dtype x_dt, int64_t M, int64_t K,
+                                     sq_norm norm, const float* gamma, const float* beta, float eps, float tau,
+                                     const void* w, sq_dtype w_dt, const int8_t* wq, const float* w_scale,
+                                     int64_t N, const float* bias, void* y, sq_dtype y_dt, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* sq_status_string(sq_status s);

@@ -26,7 +26,7 @@ def test_header_declares_the_calls():
                            "smoothquant_fold_per_tensor", "sq_norm_quant_fp8", "smoothquant_fold_fp8",
                            "sq_fp8_gemm", "sq_norm_quant_fp8_per_tensor", "sq_norm_quant_fp8_static",
                            "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor", "sq_llm_int8_workspace",
-                           "sq_llm_int8_linear", "sq_status_string"}
+                           "sq_llm_int8_linear", "sq_llm_int8_linear_noalloc", "sq_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = sq.status_string(code)
         assert s.startswith("SQ_")
     assert sq.status_string(0) == "SQ_OK"
@@ -117,6 +117,23 @@ def llm(x=A, dt=1, m=16, k=512, norm=1, g=None, b=None, eps=1e-5, tau=6.0, w=A, 
         bias=None, y=A, ydt=1, work=WS, nbytes=WS_NEED):
     return L.sq_llm_int8_linear(x, dt, m, k, norm, g, b, F(eps), F(tau), w, wdt, wq, ws, n, bias, y, ydt, work,
                                 nbytes, None)
+
+
+def llm_na(x=A, dt=1, m=16, k=512, norm=1, g=None, b=None, eps=1e-5, tau=6.0, w=A, wdt=1, wq=A, ws=A, n=64,
+           bias=None, y=A, ydt=1):
+    return L.sq_llm_int8_linear_noalloc(x, dt, m, k, norm, g, b, F(eps), F(tau), w, wdt, wq, ws, n, bias, y, ydt, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: llm_na(x=None), 1), (lambda: llm_na(y=None), 1), (lambda: llm_na(dt=3), 2), (lambda: llm_na(ydt=3), 2),
+    (lambda: llm_na(m=0), 3), (lambda: llm_na(k=100), 3), (lambda: llm_na(x=A4), 4), (lambda: llm_na(tau=-2.0), 5),
+    (lambda: llm_na(norm=2, b=A), 5),
+    # beyond the fixed scratch: refused before any device call
+    (lambda: llm_na(m=64, k=9216, n=9216), 8), (lambda: llm_na(m=8192, k=20480, n=81920), 8),
+])
+def test_noalloc_rejects_before_launch(call, code):
+    assert sq.sq_llm_int8_workspace(64, 9216, 9216)["total"] > sq.SQ_NOALLOC_SCRATCH_BYTES
+    assert call() == code
 
 
 def test_llm_int8_workspace_layout():

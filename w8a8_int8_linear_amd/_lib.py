@@ -28,7 +28,9 @@ EXPORTS = ("smoothquant_calibrate", "smoothquant_fold", "sq_norm_quant", "sq_w8a
            "sq_norm_quant_per_tensor", "sq_norm_quant_static", "sq_static_step", "smoothquant_fold_per_tensor",
            "sq_norm_quant_fp8", "smoothquant_fold_fp8", "sq_fp8_gemm", "sq_norm_quant_fp8_per_tensor",
            "sq_norm_quant_fp8_static", "sq_static_step_fp8", "smoothquant_fold_fp8_per_tensor",
-           "sq_llm_int8_workspace", "sq_llm_int8_linear", "sq_status_string")
+           "sq_llm_int8_workspace", "sq_llm_int8_linear", "sq_llm_int8_linear_noalloc", "sq_status_string")
+SQ_NOALLOC_SCRATCH_BYTES = 134217728
+SQ_ERR_TOO_LARGE = 8
 
 LLM_INT8_FIELDS = ("total", "count", "idx", "absmax", "gamma_m", "beta_m", "stats", "xq", "x_scale", "x16", "w16",
                    "deq")
@@ -67,6 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smoothquant_fold_fp8_per_tensor.argtypes = [P, P, I, I64, I64, D, F, I, P, P, P, P, P, P, P, P]
     lib.sq_llm_int8_workspace.argtypes = [I64, I64, I64, ctypes.POINTER(_LlmLayout)]
     lib.sq_llm_int8_linear.argtypes = [P, I, I64, I64, I, P, P, F, F, P, I, P, P, I64, P, P, I, P, ctypes.c_uint64, P]
+    lib.sq_llm_int8_linear_noalloc.argtypes = [P, I, I64, I64, I, P, P, F, F, P, I, P, P, I64, P, P, I, P]
     lib.sq_status_string.argtypes = [I]
     lib.sq_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -350,3 +353,29 @@ def llm_int8_parts(workspace, m, n, k, w_dtype=torch.float16):
             "xq": view("xq", torch.int8, m * k).view(m, k), "x_scale": view("x_scale", torch.float32, m),
             "x16": view("x16", half, m * p).view(m, p), "w16": view("w16", half, n * p).view(n, p),
             "deq": view("deq", torch.float32, m * n).view(m, n)}
+
+
+def sq_llm_int8_linear_noalloc(x, w, wq, w_scale, norm="none", gamma=None, beta=None, eps=1e-5, tau=6.0, bias=None,
+                               out_dtype=torch.float16, y=None):
+    """sq_llm_int8_linear with the library's fixed device scratch as its workspace (no allocation in the
+    call; y is allocated here only when None). Shapes whose workspace exceeds SQ_NOALLOC_SCRATCH_BYTES
+    raise SmoothQuantError (SQ_ERR_TOO_LARGE)."""
+    _dev(x, "x", _ACT)
+    _dev(w, "w", _ACT)
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs w {tuple(w.shape)}")
+    _dev(wq, "wq", torch.int8, (n, k))
+    _dev(w_scale, "w_scale", torch.float32, (n,))
+    _dev(gamma, "gamma", torch.float32, (k,))
+    _dev(beta, "beta", torch.float32, (k,))
+    _dev(bias, "bias", torch.float32, (n,))
+    if y is None:
+        y = torch.empty(m, n, dtype=out_dtype, device=x.device)
+    _dev(y, "y", out_dtype, (m, n))
+    with torch.cuda.device(x.device):
+        _check("sq_llm_int8_linear_noalloc", lib.sq_llm_int8_linear_noalloc(
+            _ptr(x), _DT[x.dtype], m, k, _NORM[norm], _ptr(gamma), _ptr(beta), eps, float(tau), _ptr(w), _DT[w.dtype],
+            _ptr(wq), _ptr(w_scale), n, _ptr(bias), _ptr(y), _DT[y.dtype], _stream(x)))
+    return y

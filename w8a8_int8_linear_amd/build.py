@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libsmoothquant.so")
 ARCH = os.environ.get("SQ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["sq_validate.cpp", "sq_api.cpp", "k_rows.hip", "k_rows_tensor.hip", "k_rows_step.hip", "k_rows_fp8.hip",
-           "k_rows_fp8_step.hip", "k_gemm.hip", "k_llm_int8.hip"]
+           "k_rows_fp8_step.hip", "k_gemm.hip", "k_llm_int8.hip", "sq_noalloc.hip"]
 
 # Numerics: no contraction of separate roundings, IEEE fp32 divide/sqrt, binary32
 # denormals kept. Packed fp32 instructions are disabled for all device code.

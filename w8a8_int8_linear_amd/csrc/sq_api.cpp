@@ -236,6 +236,8 @@ const char* sq_status_string(sq_status s) {
     case SQ_ERR_BAD_ARG: return "SQ_ERR_BAD_ARG: alpha, eps, norm or pointer combination not allowed";
     case SQ_ERR_UNSUPPORTED: return "SQ_ERR_UNSUPPORTED: not implemented by this build";
     case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime refused a launch";
+    case SQ_ERR_TOO_LARGE:
+      return "SQ_ERR_TOO_LARGE: the call needs more than the SQ_NOALLOC_SCRATCH_BYTES (128 MiB) of fixed scratch";
   }
   return "unknown sq_status";
 }
