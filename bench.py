@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--m", type=int, default=None, help="token count (workloads with several)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true", help="leave out the decode GEMM block")
+    p.add_argument("--no-clock", action="store_true", help="leave out the shader-clock sampling")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration runs)")
@@ -85,18 +86,77 @@ def parse():
 # ----------------------------------------------------------------------------- counter summaries
 
 GEMM_SOURCES = ["w8a8_int8_linear_amd/csrc/k_gemm.hip", "w8a8_int8_linear_amd/csrc/sq_device.h",
-                "w8a8_int8_linear_amd/build.py"]
+                "w8a8_int8_linear_amd/csrc/sq_launch.h"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "k_gemm_tile_traffic.json")
 
 
+def build_flags():
+    """The compile flags of the library (the COMMON list of its build script, loaded by path)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_sq_build_flags", os.path.join(ROOT, "w8a8_int8_linear_amd",
+                                                                                "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [f for f in mod.COMMON if not f.startswith(("-I", "/"))]
+
+
 def gemm_source_hash() -> str:
-    """Hash of everything that shapes the GEMM kernel's code (sources and build flags)."""
+    """Hash of everything that shapes the GEMM kernel's code: its sources and the compile flags."""
     import hashlib
     h = hashlib.sha256()
     for rel in GEMM_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(json.dumps(build_flags()).encode())
     return h.hexdigest()
+
+
+class ClockSampler:
+    """The GPU's current shader clock, read from the driver's sysfs DPM table (pp_dpm_sclk: the line
+    marked '*' holds the current clock, which the driver updates continuously) from a host thread
+    every ~2 ms while a workload runs: a same-run measure of the clock the GEMM holds. (The
+    gpu-metrics table behind amdsmi refreshes only every few hundred ms on this driver, so it is
+    not used.)"""
+
+    def __init__(self, path=None):
+        import glob
+        paths = [path] if path else sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(paths) != 1:
+            raise RuntimeError(f"expected one pp_dpm_sclk, found {paths}")
+        self.path = paths[0]
+        self.samples = []
+
+    def read_mhz(self):
+        with open(self.path) as f:
+            for line in f:
+                if "*" in line:
+                    return float(line.split(":", 1)[1].split("Mhz")[0].strip())
+        raise RuntimeError("no current level in pp_dpm_sclk")
+
+    def run_while(self, torch, fn, seconds):
+        """Call fn() repeatedly for about `seconds` (each call drained before the next) while sampling."""
+        import threading
+        stop = threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    self.samples.append(self.read_mhz())
+                except Exception:          # a failed read is skipped, not invented
+                    pass
+                time.sleep(0.002)
+        th = threading.Thread(target=loop, daemon=True)
+        fn()
+        torch.cuda.synchronize()
+        self.samples.clear()
+        th.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            fn()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        return self.samples
 
 
 def recorded_traffic():
@@ -179,11 +239,11 @@ def summarize_counters(trace_dir, fetch_dir, write_dir, clock_dir=None):
         wb = counters["WRITE_SIZE"]["per"][(wd, _)] * scale["WRITE_SIZE"] * 1024
         launches.append({"fetch_bytes": fb, "write_bytes": wb})
     cmd_trace = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- "
-                 "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline")
+                 "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-decode --no-clock")
     cmd_pmc = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o run --output-format csv -- "
-               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-probe-mib 1024")
+               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-clock --copy-probe-mib 1024")
     cmd_clock = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES -d <dir> -o run "
-                 "--output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline")
+                 "--output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-decode --no-clock")
     rec = {"kernel": "k_gemm_tile", "workload": "mtnlg530b_width_m8192_h20480 (fc1 then fc2)",
            "source_sha256": gemm_source_hash(), "fetch_scale": scale["FETCH_SIZE"],
            "write_scale": scale["WRITE_SIZE"], "launches": launches,
@@ -1200,6 +1260,23 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     rep = kernel_report(timer, wl, sites)
     dims = [(d["m"], d["n"], d["k"]) for d in sites]
+    clock = None
+    if not args.no_clock:
+        # the shader clock while site 0's GEMM runs back to back for about half a second
+        d0 = sites[0]
+        try:
+            sampler = ClockSampler()
+            mhz = sampler.run_while(torch, lambda: sq.sq_w8a8_gemm(d0["xq"], d0["xs"], d0["fold"]["wq"],
+                                                                   d0["fold"]["w_scale"], y=d0["y"],
+                                                                   out_dtype=d0["y"].dtype), 0.6)
+            mhz.sort()
+            clock = {"source": "sysfs pp_dpm_sclk current level, sampled every ~2 ms during back-to-back "
+                               f"launches of the {d0['m']}x{d0['n']}x{d0['k']} GEMM after the timed steps",
+                     "samples": len(mhz), "median_GHz": round(mhz[len(mhz) // 2] / 1e3, 3) if mhz else None,
+                     "min_GHz": round(mhz[0] / 1e3, 3) if mhz else None,
+                     "max_GHz": round(mhz[-1] / 1e3, 3) if mhz else None}
+        except Exception as e:        # no clock reading on this host: say so
+            clock = {"error": f"{type(e).__name__}: {e}"}
     del sites
     torch.cuda.empty_cache()
     decode = None if args.no_decode else decode_block(torch, sq)
@@ -1211,7 +1288,7 @@ def main():
     alg_bytes = [dn * dk + 4 * dn + dm * dk + 4 * dm + osize * dm * dn for dm, dn, dk in dims]
     rec = recorded_traffic() if args.workload == 5 and m == 8192 else None
     traffic = rec["traffic_bytes_per_launch"] if rec else None
-    sclk = rec.get("sclk_GHz") if rec else None
+    sclk = clock.get("median_GHz") if clock else None
     peak_sclk = PEAK_INT8_TOPS * sclk / PEAK_SCLK_GHZ if sclk else None
     out = {
         "metric": "W8A8 GEMM TOPS + % INT8 MFMA peak; norm+quant kernel HBM GB/s",
@@ -1225,9 +1302,12 @@ def main():
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": traffic, "traffic_unit": "HBM bytes per launch",
                      "sclk_GHz": round(sclk, 3) if sclk else None,
+                     "sclk_measured": clock,
                      "peak_at_sclk": round(peak_sclk, 1) if sclk else None,
                      "frac_at_sclk": round(achieved / peak_sclk, 4) if sclk else None,
-                     "mfma_busy": round(rec["mfma_busy"], 3) if rec and "mfma_busy" in rec else None,
+                     "counter_record": ({"sclk_GHz": round(rec["sclk_GHz"], 3), "mfma_busy": round(rec["mfma_busy"], 3),
+                                         "file": "profiles/k_gemm_tile_traffic.json"}
+                                        if rec and "mfma_busy" in rec else None),
                      "algorithmic_bytes_per_launch": sum(alg_bytes) / len(alg_bytes),
                      "ops_per_launch": sum(g_ops) / len(g_ops)},
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

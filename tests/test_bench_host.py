@@ -123,3 +123,12 @@ def test_prefill_summary_splits_runs_by_launch_count(scratch_root, monkeypatch):
     _write_csv(scratch_root / "pf2" / "run_kernel_trace.csv", header, rows)
     with pytest.raises(SystemExit):
         bench.summarize_prefill(str(scratch_root / "pf2"))
+
+
+def test_clock_sampler_reads_the_current_dpm_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1788Mhz *\n2: 2400Mhz\n")
+    assert bench.ClockSampler(str(f)).read_mhz() == 1788.0
+    f.write_text("0: 500Mhz\n1: 573Mhz\n2: 2400Mhz\n")
+    with pytest.raises(RuntimeError):
+        bench.ClockSampler(str(f)).read_mhz()
