@@ -185,7 +185,11 @@ GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 
                # up to 4 tokens: the MFMA decode kernel below N = 16384, the GEMV from there; K tails inside a
                # 256-byte segment, ragged N
                (3, 130, 320), (4, 16400, 1216), (2, 77, 704), (1, 1000, 4160),
-               (1, 16400, 4160), (2, 16390, 704), (3, 20000, 320), (4, 16384, 64)]
+               (1, 16400, 4160), (2, 16390, 704), (3, 20000, 320), (4, 16384, 64),
+               # 1-2 tokens: the row GEMV up to K = 9216 (ragged N, K not a multiple of 1024), past it the
+               # GEMV (N >= 16384) or the MFMA decode kernel
+               (1, 9217, 9216), (2, 4099, 4160), (1, 5, 64), (2, 300, 9152),
+               (1, 16400, 20480), (2, 3000, 13312)]
 
 
 @pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))

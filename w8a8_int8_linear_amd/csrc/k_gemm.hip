@@ -1116,9 +1116,126 @@ __global__ __launch_bounds__(256) void k_gemv(const int8_t* __restrict__ xq, con
   }
 }
 
+// ----------------------------------------------------------------------------- row GEMV (1-2 tokens, K <= 9216)
+
+// Decode with a handful of tokens, read the way a plain streaming kernel reads:
+// each wave takes whole weight rows, one at a time, and each of its load
+// instructions covers 1 KiB of one row (lane l: bytes 16 l .. 16 l + 15 of each
+// 1024-byte chunk), so the weight stream is contiguous per instruction. Every
+// lane holds its 16-byte K chunks of all MM tokens in registers for the whole
+// kernel (CH chunks per token: K <= 1024 CH; chunks past K and tokens past M
+// are zeros), multiplies them against the row with v_dot4_i32_i8 (int32,
+// exact), and the row's 64 lane sums are added by DPP inside each 16-lane row
+// and across the four rows through scalar reads. The next row's loads are in
+// flight while a row is reduced. Waves take rows gw, gw + GW, ... (GW = all
+// waves of the grid). Lane t < M stores token t's output.
+// Row n's chunks into w; a row past the end (valid false) gets a zero-length
+// resource: its loads return zeros without touching memory, so the loads are
+// issued unconditionally and the wait counts stay exact.
+template <int MM, int CH>
+__device__ __forceinline__ void gemv_row_load(const int8_t* __restrict__ wq, int64_t n, bool valid, int K, int lane,
+                                              v4i (&w)[CH]) {
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc_n(wq + n * K, valid ? static_cast<uint32_t>(K) : 0u);
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    w[c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, static_cast<uint32_t>(1024 * c + 16 * lane),
+                                                                        0, kStreamPolicy));
+}
+
+template <int MM, int CH, int YDT>
+__device__ __forceinline__ void gemv_row_finish(const v4i (&w)[CH], const v4i (&x)[MM][CH], int64_t n, int lane,
+                                                int M, int N, float xs_lane, const float* __restrict__ ws,
+                                                const float* __restrict__ bias, void* __restrict__ y) {
+  int acc[MM];
+#pragma unroll
+  for (int t = 0; t < MM; ++t) {
+    acc[t] = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[t] = __builtin_amdgcn_sdot4(w[c][j], x[t][c][j], acc[t], false);
+  }
+  int mine = 0;
+#pragma unroll
+  for (int t = 0; t < MM; ++t) {
+    int v = acc[t];
+    v += dpp_move<kDppXor1>(v);
+    v += dpp_move<kDppXor2>(v);
+    v += dpp_move<kDppHalfMirror>(v);
+    v += dpp_move<kDppMirror>(v);
+    const int total = (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+                      (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+    if (lane == t) mine = total;
+  }
+  if (lane < M) store1<YDT>(y, N, lane, static_cast<int>(n), mine, xs_lane, ws, bias);
+}
+
+template <int MM, int CH, int YDT>
+__global__ __launch_bounds__(256) void k_gemv_rows(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                   const int8_t* __restrict__ wq, const float* __restrict__ ws,
+                                                   const float* __restrict__ bias, void* __restrict__ y, int M, int N,
+                                                   int K) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // uniform
+  const int nw = gridDim.x * 4;
+  // this lane's K chunks of every token (zeros past K or past M)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc_n(xq, static_cast<uint32_t>(M * K));
+  v4i x[MM][CH];
+#pragma unroll
+  for (int t = 0; t < MM; ++t)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int k = 1024 * c + 16 * lane;
+      const uint32_t off = (t < M && k < K) ? static_cast<uint32_t>(t * K + k) : kDecNowhere;
+      x[t][c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    }
+  const float xs_lane = (YDT != SQ_DT_I32 && lane < M) ? xs[lane] : 0.0f;   // lane t stores token t
+  int64_t n = gw;
+  if (n >= N) return;
+  v4i wa[CH], wb[CH];
+  gemv_row_load<MM, CH>(wq, n, true, K, lane, wa);
+  for (;;) {
+    const int64_t n1 = n + nw;
+    gemv_row_load<MM, CH>(wq, n1 < N ? n1 : n, n1 < N, K, lane, wb);
+    gemv_row_finish<MM, CH, YDT>(wa, x, n, lane, M, N, xs_lane, ws, bias, y);
+    if (n1 >= N) break;
+    const int64_t n2 = n1 + nw;
+    gemv_row_load<MM, CH>(wq, n2 < N ? n2 : n1, n2 < N, K, lane, wa);
+    gemv_row_finish<MM, CH, YDT>(wb, x, n1, lane, M, N, xs_lane, ws, bias, y);
+    if (n2 >= N) break;
+    n = n2;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));        // the last (empty) loads land before the wave ends
+}
+
 namespace {
 
-// Decode shapes (M <= 64). INT8 with up to 4 tokens at N >= 16384: the
+// The row GEMV's grid: two workgroups (8 waves) per CU, within what fits, at
+// most one wave per row. Measured at K = 9216 with rotating weights: one
+// workgroup per CU and two gave 15.2-15.5 us for N = 9216 and 1-2 tokens,
+// four 15.0-16.5; grids that are not a multiple of the CU count (341, 682)
+// were 1-2 us slower (uneven per-CU load). Without the next row's loads in
+// flight two tokens took 16.2-27 us.
+template <int MM, int CH, int YDT>
+hipError_t launch_rows(const GemmArgs& g, hipStream_t st) {
+  auto kern = k_gemv_rows<MM, CH, YDT>;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                                        256, 0);
+  if (e != hipSuccess) return e;
+  const int cap = max(1, cus * min(max(per_cu, 1), 2));
+  const int grid = min((g.N + 3) / 4, cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, g.xq, g.x_scale, g.wq, g.w_scale, g.bias, g.y, g.M, g.N,
+                     g.K);
+  return hipGetLastError();
+}
+
+// Decode shapes (M <= 64). INT8 with 1-2 tokens, K <= 9216 and N < 16384: the
+// row GEMV (k_gemv_rows, 15.2-15.6 us at N = 9216 against 15.9-16.3 for the
+// MFMA kernel; at N = 36864 it trails k_gemv by 1-2%). INT8 with up to 4
+// tokens at N >= 16384: the
 // vector-ALU GEMV, 16 channels per workgroup (6.8 TB/s at N = 36864, where the
 // MFMA kernel reaches 6.5). Otherwise the MFMA decode kernel (gfx950 has no
 // FP8 dot product on the vector ALUs, so FP8 always takes it) with up to 9
@@ -1136,6 +1253,10 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
     hipLaunchKernelGGL(KERN, dim3((g.N + (CH) - 1) / (CH)), dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale,   \
                        g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
     return hipGetLastError();                                                                                \
+  }
+  if (!FP8 && g.M <= 2 && g.K <= 9216 && !wide) {
+    if (g.K <= 4096) return g.M == 1 ? launch_rows<1, 4, YDT>(g, st) : launch_rows<2, 4, YDT>(g, st);
+    return g.M == 1 ? launch_rows<1, 9, YDT>(g, st) : launch_rows<2, 9, YDT>(g, st);
   }
   if (!FP8 && wide) {
     if (g.M == 1) SQ_DECODE((k_gemv<1, 3, YDT>), 16)
