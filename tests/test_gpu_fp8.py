@@ -300,8 +300,9 @@ def test_fp8_gemm_persistent_grid(shape):
 
 
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
-def test_fp8_gemm_dequantised_output(out):
-    m, n, k = 300, 520, 1280
+@pytest.mark.parametrize("mnk", [(300, 520, 1280), (257, 1030, 384)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_gemm_dequantised_output(out, mnk):
+    m, n, k = mnk
     xq = _codes((m, k), 5, 30.0)
     wq = _codes((n, k), 6, 1.0)
     rng = np.random.default_rng(7)

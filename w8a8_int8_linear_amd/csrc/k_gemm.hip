@@ -140,6 +140,50 @@ __device__ __forceinline__ void store4_pre(void* __restrict__ y, int N, int m, i
   }
 }
 
+// Outputs of two adjacent 16-column MFMA tiles j, j+1 in a 16-bit type, 16
+// bytes per lane. Lane group g = lane / 16 holds columns 4g .. 4g+3 of both
+// tiles (rows lane % 16). One v_permlane16_swap per dword exchanges the
+// tile-j values of groups 1 and 3 with the tile-(j+1) values of groups 0 and
+// 2, after which group g holds 8 consecutive outputs starting at column
+// 16 (g & 1) + 8 (g >> 1) of the pair, and one store instruction covers 64
+// contiguous bytes of each of its 16 rows (four 32-byte pieces before).
+// Measured on the 256x256 tile at K = 4096: the epilogue from 8-13 to 4-6 us
+// per tile. Same roundings as store4_pre; w0 / w1 hold the weight scales of
+// the lane's columns in tiles j and j+1 (clamped to the last column). Every
+// lane takes part in the swaps; the stores are guarded per lane.
+template <int YDT, typename AccV = v4i>
+__device__ __forceinline__ void store8_pair(void* __restrict__ y, int M, int N, int m, int nb, const AccV a0,
+                                            const AccV a1, float xs, const float (&w0)[4], const float (&w1)[4],
+                                            const float* __restrict__ bias, int lane) {
+  static_assert(YDT == SQ_DT_F16 || YDT == SQ_DT_BF16, "16-bit outputs");
+  const int g = lane >> 4;
+  uint32_t h[2][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float t0 = mul_rn(mul_rn(static_cast<float>(a0[r]), xs), w0[r]);
+    float t1 = mul_rn(mul_rn(static_cast<float>(a1[r]), xs), w1[r]);
+    if (bias) {
+      t0 = add_rn(t0, bias[min(nb + 4 * g + r, N - 1)]);
+      t1 = add_rn(t1, bias[min(nb + 16 + 4 * g + r, N - 1)]);
+    }
+    h[0][r] = (YDT == SQ_DT_F16) ? f32_to_f16_rne(t0) : f32_to_bf16_rne(t0);
+    h[1][r] = (YDT == SQ_DT_F16) ? f32_to_f16_rne(t1) : f32_to_bf16_rne(t1);
+  }
+  const auto lo = __builtin_amdgcn_permlane16_swap(h[0][0] | (h[0][1] << 16), h[1][0] | (h[1][1] << 16), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(h[0][2] | (h[0][3] << 16), h[1][2] | (h[1][3] << 16), false, false);
+  const uint32_t d[4] = {lo[0], hi[0], lo[1], hi[1]};
+  const int c = nb + 16 * (g & 1) + 8 * (g >> 1);
+  if (m >= M) return;
+  uint16_t* p = static_cast<uint16_t*>(y) + static_cast<int64_t>(m) * N + c;
+  if (c + 7 < N && (N & 7) == 0) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(d[0], d[1], d[2], d[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c + e < N) p[e] = static_cast<uint16_t>(d[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
 // ----------------------------------------------------------------------------- tiled kernel
 
 constexpr int kTile = 256;                     // output tile edge (m and n)
@@ -340,15 +384,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_k64(const int8_t* __restri
   __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0): no DMA into LDS outlives the loop
 
   // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
+  if constexpr (YDT == SQ_DT_F16 || YDT == SQ_DT_BF16) {
+    float wv[TJ][4];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int m = m0 + wm + 16 * i + (lane & 15);
-    if (m >= M) continue;
-    const float xsm = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
-      if (n < N) store4<YDT>(y, N, m, n, acc[i][j], xsm, ws, bias);
+      for (int r = 0; r < 4; ++r) wv[j][r] = ws[min(n0 + wn + 16 * j + 4 * (lane >> 4) + r, N - 1)];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = m0 + wm + 16 * i + (lane & 15);
+      const float xsm = xs[min(m, M - 1)];
+#pragma unroll
+      for (int j = 0; j < TJ; j += 2)
+        store8_pair<YDT>(y, M, N, m, n0 + wn + 16 * j, acc[i][j], acc[i][j + 1], xsm, wv[j], wv[j + 1], bias, lane);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = m0 + wm + 16 * i + (lane & 15);
+      if (m >= M) continue;
+      const float xsm = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+        if (n < N) store4<YDT>(y, N, m, n, acc[i][j], xsm, ws, bias);
+      }
     }
   }
 }
@@ -593,14 +653,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
     }
 
     // Epilogue: lane holds acc[m = .. + lane % 16][n = .. + 4 (lane / 16) + r].
+    if constexpr (YDT == SQ_DT_F16 || YDT == SQ_DT_BF16) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int m = cm0 + wm + 16 * i + (lane & 15);
-      if (m >= M) continue;
+      for (int i = 0; i < TI; ++i) {
+        const int m = cm0 + wm + 16 * i + (lane & 15);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
-        if (n < N) store4_pre<YDT>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
+        for (int j = 0; j < TJ; j += 2)
+          store8_pair<YDT>(y, M, N, m, cn0 + wn + 16 * j, acc[i][j], acc[i][j + 1], xsv[i], wv[j], wv[j + 1], bias,
+                           lane);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int m = cm0 + wm + 16 * i + (lane & 15);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
+          if (n < N) store4_pre<YDT>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
+        }
       }
     }
     if (!more) break;
@@ -775,14 +846,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
       setup(vn);
       prologue();
     }
+    if constexpr (YDT == SQ_DT_F16 || YDT == SQ_DT_BF16) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int m = cm0 + wm + 16 * i + (lane & 15);
-      if (m >= M) continue;
+      for (int i = 0; i < TI; ++i) {
+        const int m = cm0 + wm + 16 * i + (lane & 15);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
-        if (n < N) store4_pre<YDT, v4f>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
+        for (int j = 0; j < TJ; j += 2)
+          store8_pair<YDT, v4f>(y, M, N, m, cn0 + wn + 16 * j, acc[i][j], acc[i][j + 1], xsv[i], wv[j], wv[j + 1],
+                                bias, lane);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int m = cm0 + wm + 16 * i + (lane & 15);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
+          if (n < N) store4_pre<YDT, v4f>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
+        }
       }
     }
     if (!more) break;
