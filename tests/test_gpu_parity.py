@@ -226,7 +226,11 @@ def test_gemm_decode_every_token_count(m, nk):
 # More tiles than resident workgroups: the prefill kernel's workgroups loop over several tiles (each
 # tile's epilogue overlapping the next tile's first stages), with ragged last tile-rows and -columns.
 # Every tile-row is sampled (every 16th row and the edges) against all columns.
-PERSIST_SHAPES = [(2100, 8000, 256), (4097, 16385, 128), (1100, 30000, 384)]
+# The launch picks the tile width (256, 192 or 128 columns) whose grid wastes least of its last wave:
+# 2100 x 8000, 4097 x 16385 and 257 x 33000 take 192-column tiles, 1281 x 10760 and 513 x 32648
+# 128-column ones (2 and 3 tiles per workgroup), the rest 256.
+PERSIST_SHAPES = [(2100, 8000, 256), (4097, 16385, 128), (1100, 30000, 384), (257, 33000, 256), (1281, 10760, 256),
+                  (513, 32648, 128)]
 
 
 def _persist_rows(m):
@@ -246,8 +250,9 @@ def test_gemm_persistent_grid_accumulators(mnk):
 
 
 @pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
-def test_gemm_persistent_grid_dequant_with_bias(out):
-    m, n, k = 2100, 8000, 256
+@pytest.mark.parametrize("mnk", [(2100, 8000, 256), (1281, 10760, 256)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_persistent_grid_dequant_with_bias(out, mnk):
+    m, n, k = mnk
     xq, wq = rand_int8((m, k), 810), rand_int8((n, k), 910)
     xs, ws = rand_positive(m, 820, 1e-3, 0.5), rand_positive(n, 920, 1e-4, 0.05)
     b = rand_tokens(1, n, "f32", 930)[0]

@@ -494,15 +494,77 @@ __device__ __forceinline__ void interleave2(bool with_dma) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int YDT>
+// The tile's width in N as MFMA tiles per wave, TJN: 4 (256 columns), 3 (192)
+// or 2 (128). The eight waves stay 2 x 4, each 128 tokens x 16 TJN channels,
+// and a stage's wq rows take TJN DMA instructions per wave. Narrower tiles
+// serve short grids: a width whose tile count fills whole waves of the CUs
+// wastes less of the last wave (OPT-6.7B's QKV, 2048 x 12288: 384 tiles of
+// 256 x 256 are 1.5 waves on 256 CUs, 512 tiles of 256 x 192 are two).
+template <int TJN>
+struct FragsN {
+  v4i a[TI], b[TJN];
+};
+
+// Stage rows of one operand: N DMA instructions per wave (8 rows x 128 bytes each).
+template <int N>
+__device__ __forceinline__ void issue_rows2(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds, const uint32_t* off, int k0,
+                                            int wid) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wid * N + i) * 1024), 16, off[i], k0, 0, 0);
+}
+
+template <int TJN>
+__device__ __forceinline__ void read_frags2n(const int8_t* la, const int8_t* lb, const int (&a_rd)[2],
+                                             const int (&b_rd)[2], int t, FragsN<TJN>& f) {
+#pragma unroll
+  for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const v4i*>(la + a_rd[t] + i * 16 * kSlice2);
+#pragma unroll
+  for (int j = 0; j < TJN; ++j) f.b[j] = *reinterpret_cast<const v4i*>(lb + b_rd[t] + j * 16 * kSlice2);
+}
+
+template <int TJN>
+__device__ __forceinline__ void mma_n(const FragsN<TJN>& f, v4i (&acc)[TI][TJN]) {
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// interleave2 for any width: the step's MFMAs spread evenly over its fragment
+// reads (1-3 after each), the refill's DMAs two at a time after every third
+// read. TJN = 4 keeps interleave2's schedule.
+template <int TJN>
+__device__ __forceinline__ void interleave2n(bool with_dma) {
+  if constexpr (TJN == 4) {
+    interleave2(with_dma);
+  } else {
+    constexpr int NR = TI + TJN, NM = TI * TJN, ND = kDma2PerWave + TJN;
+    static_assert(NM >= NR && NM <= 3 * NR && (ND + 1) / 2 <= (NR + 2) / 3, "schedule shape");
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (with_dma && i % 3 == 0 && i / 3 < (ND + 1) / 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int c = (i + 1) * NM / NR - i * NM / NR;
+      if (c == 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      else if (c == 2) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int YDT, int TJN = 4>
 __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                                       const int8_t* __restrict__ wq, const float* __restrict__ ws,
                                                       const float* __restrict__ bias, void* __restrict__ y, int M,
                                                       int N, int K, int tiles_m, int tiles_n, int group) {
   __shared__ __attribute__((aligned(1024))) int8_t lA0[kStage2Bytes];
   __shared__ __attribute__((aligned(1024))) int8_t lA1[kStage2Bytes];
-  __shared__ __attribute__((aligned(1024))) int8_t lB0[kStage2Bytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lB0[kStage2Bytes];   // 64 TJN of its 256 rows used
   __shared__ __attribute__((aligned(1024))) int8_t lB1[kStage2Bytes];
+  constexpr int kTN = 64 * TJN;                      // tile width in N
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: LDS bases stay scalar
@@ -516,13 +578,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   // slot lane % 8, which holds chunk slot ^ swz2(row). Rows past M or N
   // re-read the last row (never stored).
   int m0 = 0, n0 = 0;
-  uint32_t a_off[kDma2PerWave], b_off[kDma2PerWave];
+  uint32_t a_off[kDma2PerWave], b_off[TJN];
   __amdgpu_buffer_rsrc_t ra, rb;
   auto setup = [&](int v) {
     int tm, tn;
     map_tile(v, ntiles, tiles_m, group, tm, tn);
     m0 = tm * kTile;
-    n0 = tn * kTile;
+    n0 = tn * kTN;
     // recomputed per tile from the lane id read afresh (mbcnt in volatile asm
     // cannot be hoisted): kept across the tile loop, these per-lane offsets
     // would hold registers the loop needs
@@ -533,6 +595,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
       const int r = (wid * kDma2PerWave + i) * 8 + (ln >> 3);
       const int c = (ln & 7) ^ swz2(r);
       a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
+    }
+#pragma unroll
+    for (int i = 0; i < TJN; ++i) {
+      const int r = (wid * TJN + i) * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz2(r);
       b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
     }
     ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
@@ -540,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   };
 
   // Fragment reads of K step t: row R = base + 16 i + lane % 16, chunk 4 t + lane / 16.
-  const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
+  const int wm = (wid & 1) * 128, wn = (wid >> 1) * (16 * TJN);
   const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
   int a_rd[2], b_rd[2];
 #pragma unroll
@@ -562,58 +629,60 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
   const int last = (ns - 1) * kSlice2;
   auto prologue = [&]() {
     // in stage order: the waits count DMAs in issue order (see the 64-byte kernel)
-    issue_stage2(ra, lA0, a_off, 0, wid);
-    issue_stage2(rb, lB0, b_off, 0, wid);
+    issue_rows2<kDma2PerWave>(ra, lA0, a_off, 0, wid);
+    issue_rows2<TJN>(rb, lB0, b_off, 0, wid);
     memory_opaque();
-    issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
-    issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
+    issue_rows2<kDma2PerWave>(ra, lA1, a_off, min(kSlice2, last), wid);
+    issue_rows2<TJN>(rb, lB1, b_off, min(kSlice2, last), wid);
   };
   int v = blockIdx.x;
   setup(v);
   prologue();
 
   for (;;) {
-    v4i acc[TI][TJ];
+    v4i acc[TI][TJN];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-    Frags f0, f1;
-    // vmcnt(8): stage 0 landed. Loads complete in issue order, so with at most
-    // 8 operations outstanding no load of stage 0 can be (the previous tile's
+      for (int j = 0; j < TJN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    FragsN<TJN> f0, f1;
+    // vmcnt(kStageDma): stage 0 landed. Loads complete in issue order, so with
+    // at most as many operations outstanding as stage 1 issued (4 + TJN DMA
+    // instructions per wave) no load of stage 0 can be (the previous tile's
     // stores, issued after these DMAs, are waited for as well).
-    __builtin_amdgcn_s_waitcnt(0x0F78);
+    constexpr int kStageDma = kDma2PerWave + TJN;
+    __builtin_amdgcn_s_waitcnt((kStageDma & 15) | ((kStageDma >> 4) << 14) | 0x0F70);
     stage_barrier();
     {
       // in asm: across the tile loop's back edge the compiler's own waits would
       // also drain stage 1 and the previous tile's stores (vmcnt(0))
-      uint32_t addr[TI + TJ];
-      v4i r[TI + TJ];
+      uint32_t addr[TI + TJN];
+      v4i r[TI + TJN];
 #pragma unroll
       for (int i = 0; i < TI; ++i) addr[i] = lds_addr(lA0) + a_rd[0] + i * 16 * kSlice2;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) addr[TI + j] = lds_addr(lB0) + b_rd[0] + j * 16 * kSlice2;
+      for (int j = 0; j < TJN; ++j) addr[TI + j] = lds_addr(lB0) + b_rd[0] + j * 16 * kSlice2;
       lds_read_frags(r, addr);
 #pragma unroll
       for (int i = 0; i < TI; ++i) f0.a[i] = r[i];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) f0.b[j] = r[TI + j];
+      for (int j = 0; j < TJN; ++j) f0.b[j] = r[TI + j];
     }
 
 #define SQ_STAGE(LA_CUR, LB_CUR, LA_NXT, LB_NXT)                                      \
   {                                                                                   \
-    read_frags2(LA_CUR, LB_CUR, a_rd, b_rd, 1, f1);                                   \
-    mma(f0, acc);                                                                     \
-    interleave2(false);                                                               \
+    read_frags2n(LA_CUR, LB_CUR, a_rd, b_rd, 1, f1);                                  \
+    mma_n(f0, acc);                                                                   \
+    interleave2n<TJN>(false);                                                         \
     __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0) */                     \
     stage_barrier();                                                                  \
     const int kn = min((s + 2) * kSlice2, last);                                      \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    issue_stage2(ra, LA_CUR, a_off, kn, wid);                                         \
-    issue_stage2(rb, LB_CUR, b_off, kn, wid);                                         \
-    read_frags2(LA_NXT, LB_NXT, a_rd, b_rd, 0, f0);                                   \
-    mma(f1, acc);                                                                     \
-    interleave2(true);                                                                \
+    issue_rows2<kDma2PerWave>(ra, LA_CUR, a_off, kn, wid);                                          \
+    issue_rows2<TJN>(rb, LB_CUR, b_off, kn, wid);                                          \
+    read_frags2n(LA_NXT, LB_NXT, a_rd, b_rd, 0, f0);                                  \
+    mma_n(f1, acc);                                                                   \
+    interleave2n<TJN>(true);                                                          \
     ++s;                                                                              \
   }
     int s = 0;
@@ -628,14 +697,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
     // This tile's scales, loaded before the next tile's DMAs so that the
     // epilogue waits for these loads only (a bias is read in the epilogue).
     const int cm0 = m0, cn0 = n0;
-    float xsv[TI], wv[TJ][4];
+    float xsv[TI], wv[TJN][4];
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int m = min(cm0 + wm + 16 * i + (lane & 15), M - 1);
       xsv[i] = (YDT == SQ_DT_I32) ? 0.0f : xs[m];
     }
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+    for (int j = 0; j < TJN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int nn = min(cn0 + wn + 16 * j + 4 * (lane >> 4) + r, N - 1);
@@ -658,9 +727,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
       for (int i = 0; i < TI; ++i) {
         const int m = cm0 + wm + 16 * i + (lane & 15);
 #pragma unroll
-        for (int j = 0; j < TJ; j += 2)
+        for (int j = 0; j + 1 < TJN; j += 2)
           store8_pair<YDT>(y, M, N, m, cn0 + wn + 16 * j, acc[i][j], acc[i][j + 1], xsv[i], wv[j], wv[j + 1], bias,
                            lane);
+        if constexpr (TJN % 2 == 1) {                   // the odd last tile, four outputs per lane
+          const int n = cn0 + wn + 16 * (TJN - 1) + 4 * (lane >> 4);
+          if (m < M && n < N) store4_pre<YDT>(y, N, m, n, acc[i][TJN - 1], xsv[i], wv[TJN - 1], bias);
+        }
       }
     } else {
 #pragma unroll
@@ -668,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile(const int8_t* __restrict__
         const int m = cm0 + wm + 16 * i + (lane & 15);
         if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
+        for (int j = 0; j < TJN; ++j) {
           const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
           if (n < N) store4_pre<YDT>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
         }
@@ -1384,6 +1457,41 @@ inline hipError_t tile_grid(const void* kernel, int ntiles, int* grid) {
   return hipSuccess;
 }
 
+// Tile width for a prefill shape: the width (tiles per wave TJN = 4, 3, 2:
+// 256, 192, 128 columns) whose grid costs least, counting each wave of
+// resident workgroups at the width's measured time per tile relative to the
+// 256-column tile.
+constexpr float kTileCost[5] = {0.0f, 0.0f, 0.60f, 0.81f, 1.0f};
+inline hipError_t tile_width(int M, int N, int* tjn) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int tiles_m = (M + kTile - 1) / kTile;
+  float best = 0.0f;
+  *tjn = 4;
+  for (int t = 4; t >= 2; --t) {
+    const int tiles = tiles_m * ((N + 64 * t - 1) / (64 * t));
+    const float cost = static_cast<float>((tiles + cus - 1) / cus) * kTileCost[t];
+    if (t == 4 || cost < best) {
+      best = cost;
+      *tjn = t;
+    }
+  }
+  return hipSuccess;
+}
+
+template <int YDT, int TJN>
+hipError_t launch_tile(const GemmArgs& g, int tiles_m, int group, hipStream_t st) {
+  const int tiles_n = (g.N + 64 * TJN - 1) / (64 * TJN);
+  int grid = 0;
+  if (hipError_t e = tile_grid(reinterpret_cast<const void*>(k_gemm_tile<YDT, TJN>), tiles_m * tiles_n, &grid))
+    return e;
+  hipLaunchKernelGGL((k_gemm_tile<YDT, TJN>), dim3(grid), dim3(512), 0, st, g.xq, g.x_scale, g.wq, g.w_scale, g.bias,
+                     g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  return hipGetLastError();
+}
+
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) return launch_decode<YDT, false>(g, st);
@@ -1391,10 +1499,11 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
   if (g.K % kSlice2 == 0) {
-    int grid = 0;
-    if (hipError_t e = tile_grid(reinterpret_cast<const void*>(k_gemm_tile<YDT>), tiles_m * tiles_n, &grid)) return e;
-    hipLaunchKernelGGL((k_gemm_tile<YDT>), dim3(grid), dim3(512), 0, st, g.xq, g.x_scale, g.wq, g.w_scale, g.bias,
-                       g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+    int tjn = 4;
+    if (hipError_t e = tile_width(g.M, g.N, &tjn)) return e;
+    if (tjn == 3) return launch_tile<YDT, 3>(g, tiles_m, group, st);
+    if (tjn == 2) return launch_tile<YDT, 2>(g, tiles_m, group, st);
+    return launch_tile<YDT, 4>(g, tiles_m, group, st);
   } else
     hipLaunchKernelGGL((k_gemm_tile_k64<YDT>), dim3(tiles_m * tiles_n), dim3(512), 0, st, g.xq, g.x_scale, g.wq,
                        g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
