@@ -483,7 +483,7 @@ def summarize_ln_counters(pmc_dir, m=8192, k=20480):
     if not per:
         raise SystemExit("no LayerNorm quantiser dispatch in the run")
     cmd = ("rocprofv3 --pmc SQ_INSTS_VALU GRBM_GUI_ACTIVE -d <dir> -o run --output-format csv -- "
-           "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline")
+           "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-decode --no-clock")
     lines = ["# LayerNorm quantiser vector-ALU issue (rocprofv3 --pmc): MT-NLG width, 8192 x 20480 fp16", "",
              f"Command: `{cmd}`, then `python bench.py --summarize-ln-counters <dir>`.", "",
              "Kernel `sq::k_norm_quant<sq::f16_t, 1, 5, 512, 0>` (LayerNorm, per-token INT8 steps). Clock = "

@@ -23,15 +23,19 @@ namespace sq {
 template <typename T, int NV, int THREADS>
 struct RawRow {
   Raw8<T> r[NV];
+  // byte offset of the thread's vector i within a row
+  static __device__ __forceinline__ uint32_t off(int i) {
+    return static_cast<uint32_t>(threadIdx.x + i * THREADS) * (8 * Storage<T>::kBytes);
+  }
+  // buffer resource of row `row` (uniform)
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* x, int64_t row, int K) {
+    return buf_rsrc(static_cast<const char*>(x) + row * K * Storage<T>::kBytes,
+                    static_cast<uint32_t>(K) * Storage<T>::kBytes);
+  }
   __device__ __forceinline__ void load(const void* x, int64_t row, int K) {
-    const char* xrow = static_cast<const char*>(x) + row * K * Storage<T>::kBytes;
-    const int nvec = K >> 3;
+    const __amdgpu_buffer_rsrc_t rr = rsrc(x, row, K);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int vi = threadIdx.x + i * THREADS;
-      if (vi < nvec) raw_load<T>(xrow + static_cast<size_t>(vi) * 8 * Storage<T>::kBytes, r[i]);
-      else r[i] = Raw8<T>{};   // padding: zeros, never reloaded
-    }
+    for (int i = 0; i < NV; ++i) raw_load_buf<T>(rr, off(i), r[i]);   // padding vectors read zeros
   }
 };
 
@@ -54,6 +58,11 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
                                               const float* __restrict__ beta, float eps, RedRing<THREADS>& red,
                                               int& rk, float* __restrict__ st = nullptr) {
   const int nvec = K >> 3;
+  // 1/K in binary64, the same for every row: a product with it is within 2^-52
+  // relative of the quotient, far inside the 2^-12-spacing near-tie margin of
+  // the binary32 statistics (a division per row cost two binary64 divide
+  // sequences of every wave)
+  const double inv_k = 1.0 / static_cast<double>(K);
   float mu = 0.0f, r = 1.0f;
   if constexpr (NORM == SQ_NORM_LAYERNORM) {
     // One pass: S1 = sum x and S2' = sum x^2 (per-vector partial sums,
@@ -84,7 +93,7 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
       sq += q1[i];
     }
     block_sum2<THREADS>(s1, sq, red.at(rk++));
-    const double mean = s1 / static_cast<double>(K);
+    const double mean = s1 * inv_k;
     const double cross = s1 * mean;
     double s2;
     if (cross <= sq * (1.0 - 1.0 / 256.0)) {                 // workgroup-uniform
@@ -112,7 +121,7 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
       s2 = block_sum<THREADS>(s2, red.at(rk++));
     }
     mu = static_cast<float>(mean);
-    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
+    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 * inv_k), eps)));
   } else if constexpr (NORM == SQ_NORM_RMSNORM) {
     double p2[NV];
 #pragma unroll
@@ -128,22 +137,24 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
 #pragma unroll
     for (int i = 0; i < NV; ++i) s2 += p2[i];
     s2 = block_sum<THREADS>(s2, red.at(rk++));
-    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 / static_cast<double>(K)), eps)));
+    r = div_rn(1.0f, sqrt_rn(add_rn(static_cast<float>(s2 * inv_k), eps)));
   }
   if (st != nullptr && threadIdx.x == 0) {
     st[0] = mu;
     st[1] = r;
   }
-  const float* gp = gamma ? gamma : kOnes8;
-  const float* bp = beta ? beta : kZeros8;
-  const int gmask = gamma ? -1 : 0, bmask = beta ? -1 : 0;
+  // gamma / beta through buffer resources (uniform) at per-thread offsets that
+  // are the same for every row; a missing one reads the stand-in at offset 0
+  const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gamma ? gamma : kOnes8, gamma ? 4u * static_cast<uint32_t>(K) : 32u);
+  const __amdgpu_buffer_rsrc_t rb = buf_rsrc(beta ? beta : kZeros8, beta ? 4u * static_cast<uint32_t>(K) : 32u);
+  const uint32_t gmask = gamma ? ~0u : 0u, bmask = beta ? ~0u : 0u;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = threadIdx.x + i * THREADS;
     if (vi >= nvec) continue;
     float g[8], b[8];
-    load8_f32(gp + (8 * vi & gmask), g);
-    if constexpr (NORM == SQ_NORM_LAYERNORM) load8_f32(bp + (8 * vi & bmask), b);
+    load8_f32_buf(rg, (32u * static_cast<uint32_t>(vi)) & gmask, g);
+    if constexpr (NORM == SQ_NORM_LAYERNORM) load8_f32_buf(rb, (32u * static_cast<uint32_t>(vi)) & bmask, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float t = v[i][e];
@@ -250,14 +261,14 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
                                              float* __restrict__ x_scale, RedRing<THREADS>& red, int& rk,
                                              float* __restrict__ stats = nullptr) {
   const int nvec = K >> 3;
-  constexpr int B = Storage<T>::kBytes;
-  int8_t* qrow = xq + row * K;
+  using RR = RawRow<T, NV, THREADS>;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + row * K, static_cast<uint32_t>(K));   // this row's codes
   const bool refill = next < M;
-  // Address of the next row, formed unconditionally and used only when
+  // Resource of the next row, formed unconditionally and used only when
   // refill holds. (Written as refill ? next : row, ROCm 7.2's compiler turns
   // the select into an s_cselect on a stale SCC -- the 64-bit compare went to
   // VCC -- and reloads the current row.)
-  const char* nrow = static_cast<const char*>(x) + next * K * B;
+  const __amdgpu_buffer_rsrc_t rn = RR::rsrc(x, next, K);
   if constexpr (NORM == SQ_NORM_NONE) {
     // Narrow rows at up to 512 threads keep pass one's products for pass two
     // (8 NV VGPRs, within the 128 of two workgroups per CU) and refill the raw
@@ -283,7 +294,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
           const int vi = threadIdx.x + i * THREADS;
-          if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+          if (vi < nvec) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
         }
       }
     }
@@ -298,7 +309,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(ys[i]));
+        if (vi < nvec) store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.codes8(ys[i]));
       }
     } else {
       // recompute x * gamma below rather than keep pass one's 8*NV products in registers
@@ -311,8 +322,8 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
         if (vi < nvec) {
           float y[8];
           none_y(raw, i, gv, y);
-          store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(y));
-          if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+          store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.codes8(y));
+          if (refill) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
         }
       }
     }
@@ -324,7 +335,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+        if (vi < nvec) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
       }
     }
     normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk, STATS ? stats + 2 * row : nullptr);
@@ -345,7 +356,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * THREADS;
-      if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.codes8(v[i]));
+      if (vi < nvec) store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.codes8(v[i]));
     }
   }
 }
@@ -375,10 +386,10 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
                                                     RedRing<THREADS>& red, int& rk, const Q& qz,
                                                     bool write_scale) {
   const int nvec = K >> 3;
-  constexpr int B = Storage<T>::kBytes;
-  int8_t* qrow = xq + row * K;
+  using RR = RawRow<T, NV, THREADS>;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + row * K, static_cast<uint32_t>(K));
   const bool refill = next < M;
-  const char* nrow = static_cast<const char*>(x) + next * K * B;   // used only when refill holds
+  const __amdgpu_buffer_rsrc_t rn = RR::rsrc(x, next, K);          // used only when refill holds
   constexpr bool amax_only = MODE == kRowsAmax;
   float amax = 0.0f;
   if constexpr (NORM == SQ_NORM_NONE) {
@@ -398,7 +409,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
           none_y(raw, i, gv, y);
 #pragma unroll
           for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
-          if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+          if (refill) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
         }
       }
     } else if constexpr (kKeepY) {
@@ -412,13 +423,13 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
           const int vi = threadIdx.x + i * THREADS;
-          if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+          if (vi < nvec) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
         }
       }
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.template codes8<true>(ys[i]));
+        if (vi < nvec) store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.template codes8<true>(ys[i]));
       }
     } else {
 #pragma unroll
@@ -427,8 +438,8 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
         if (vi < nvec) {
           float y[8];
           none_y(raw, i, gv, y);
-          store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.template codes8<true>(y));
-          if (refill) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+          store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.template codes8<true>(y));
+          if (refill) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
         }
       }
     }
@@ -440,7 +451,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) raw_load<T>(nrow + static_cast<size_t>(vi) * 8 * B, raw.r[i]);
+        if (vi < nvec) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
       }
     }
     normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk);
@@ -453,7 +464,7 @@ __device__ __forceinline__ void quantize_row_tensor(RawRow<T, NV, THREADS>& raw,
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) store_codes8(qrow + static_cast<size_t>(vi) * 8, qz.template codes8<true>(v[i]));
+        if (vi < nvec) store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.template codes8<true>(v[i]));
       }
     }
   }

@@ -69,6 +69,34 @@ __device__ __forceinline__ void store_codes8(int8_t* p, uint2 w) {
   __builtin_nontemporal_store(u32x2_t{w.x, w.y}, reinterpret_cast<u32x2_t*>(p));
 }
 
+// Rows through buffer resources: one resource per row (its base and size are
+// workgroup-uniform, so they live in scalar registers and cost no vector
+// instructions per row), and each thread's byte offsets within a row stay the
+// same for every row. Offsets at or past `bytes` read zeros and drop writes.
+constexpr int kBufNonTemporal = 2;           // buffer cache policy: streamed once
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+template <typename T> __device__ __forceinline__ void raw_load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<T>& v) {
+  v.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNonTemporal));
+}
+template <>
+__device__ __forceinline__ void raw_load_buf<f32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<f32_t>& v) {
+  v.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNonTemporal));
+  v.b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kBufNonTemporal));
+}
+__device__ __forceinline__ void store_codes8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 w) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w.x, w.y}, r, off, 0, kBufNonTemporal);
+}
+// 8 binary32 values (gamma, beta) at byte offset off, cached normally.
+__device__ __forceinline__ void load8_f32_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, float v[8]) {
+  const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
 // Widen 8 stored elements exactly to binary32.
 template <typename T> __device__ __forceinline__ void widen8(const Raw8<T>& r, float v[8]);
 
