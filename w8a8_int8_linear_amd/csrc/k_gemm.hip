@@ -1389,7 +1389,8 @@ hipError_t launch_rows(const GemmArgs& g, hipStream_t st) {
 
 // Decode shapes (M <= 64). INT8 with 1-2 tokens, K <= 9216 and N < 16384: the
 // row GEMV (k_gemv_rows, 15.2-15.6 us at N = 9216 against 15.9-16.3 for the
-// MFMA kernel; at N = 36864 it trails k_gemv by 1-2%). INT8 with up to 4
+// MFMA kernel; at N = 36864 it trails k_gemv by 1-2%; with 4 tokens, 234
+// VGPRs, it took 16.6 us against the MFMA kernel's 16.0). INT8 with up to 4
 // tokens at N >= 16384: the
 // vector-ALU GEMV, 16 channels per workgroup (6.8 TB/s at N = 36864, where the
 // MFMA kernel reaches 6.5). Otherwise the MFMA decode kernel (gfx950 has no
