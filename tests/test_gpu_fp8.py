@@ -231,8 +231,11 @@ def test_fp8_gemm_decode_every_token_count(m, n):
 
 
 # More tiles than resident workgroups: the FP8 prefill kernel's workgroups loop over several tiles,
-# with ragged last tile-rows and -columns; sampled positions cover every tile.
-@pytest.mark.parametrize("shape", [(2100, 8000, 256), (4097, 9000, 384)], ids=lambda s: "x".join(map(str, s)))
+# with ragged last tile-rows and -columns; sampled positions cover every 256 x 128 region (the
+# narrowest tile). 2100 x 8000 takes 192-column tiles, 1281 x 10760 128-column ones (two per
+# workgroup), 4097 x 9000 256-column ones.
+@pytest.mark.parametrize("shape", [(2100, 8000, 256), (4097, 9000, 384), (1281, 10760, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_fp8_gemm_persistent_grid(shape):
     m, n, k = shape
     xq = _codes((m, k), 11 + m, 40.0)
@@ -244,10 +247,10 @@ def test_fp8_gemm_persistent_grid(shape):
     y = sq.sq_fp8_gemm(torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda(), torch.from_numpy(wq).cuda(),
                        torch.from_numpy(ws).cuda(), torch.from_numpy(bias).cuda(), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    tm, tn = np.meshgrid(np.arange(-(-m // 256)), np.arange(-(-n // 256)), indexing="ij")
+    tm, tn = np.meshgrid(np.arange(-(-m // 256)), np.arange(-(-n // 128)), indexing="ij")
     mi = np.concatenate([np.minimum(tm.ravel() * 256 + rng.integers(0, 256, tm.size), m - 1),
                          rng.integers(0, m, 2000), [0, m - 1, m - 1, 0]])
-    ni = np.concatenate([np.minimum(tn.ravel() * 256 + rng.integers(0, 256, tn.size), n - 1),
+    ni = np.concatenate([np.minimum(tn.ravel() * 128 + rng.integers(0, 128, tn.size), n - 1),
                          rng.integers(0, n, 2000), [0, n - 1, 0, n - 1]])
     acc, tol_acc = fp8_gemm_tolerance(xq, wq, mi, ni)
     scale = xs.astype(np.float64)[mi] * ws.astype(np.float64)[ni]

@@ -783,13 +783,14 @@ __device__ __forceinline__ v8i lds_frag8(const int8_t* base, int off0, int off1)
 
 // Four MFMAs of A block i against the stage's B blocks, while block i+1 is read
 // (the read goes out first, then the MFMAs, in that order).
-__device__ __forceinline__ void fp8_block(v4f (&acc)[TJ], const v8i& a, const v8i (&fb)[TJ]) {
+template <int TJN>
+__device__ __forceinline__ void fp8_block(v4f (&acc)[TJN], const v8i& a, const v8i (&fb)[TJN]) {
 #pragma unroll
-  for (int j = 0; j < TJ; ++j)
+  for (int j = 0; j < TJN; ++j)
     acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], a, acc[j], 0, 0, 0, 127, 0, 127);
 }
 
-template <int YDT>
+template <int YDT, int TJN = 4>
 __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                                                           const uint8_t* __restrict__ wq, const float* __restrict__ ws,
                                                           const float* __restrict__ bias, void* __restrict__ y, int M,
@@ -804,13 +805,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
   const int ntiles = tiles_m * tiles_n;
   // persistent over tiles b, b + G, ..., as k_gemm_tile
   int m0 = 0, n0 = 0;
-  uint32_t a_off[kDma2PerWave], b_off[kDma2PerWave];
+  uint32_t a_off[kDma2PerWave], b_off[TJN];
   __amdgpu_buffer_rsrc_t ra, rb;
   auto setup = [&](int v) {
     int tm, tn;
     map_tile(v, ntiles, tiles_m, group, tm, tn);
     m0 = tm * kTile;
-    n0 = tn * kTile;
+    n0 = tn * (64 * TJN);
     int ln;                                         // the lane id read afresh, as in k_gemm_tile
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
@@ -818,12 +819,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
       const int r = (wid * kDma2PerWave + i) * 8 + (ln >> 3);
       const int c = (ln & 7) ^ swz2(r);
       a_off[i] = static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) + 16u * c;
+    }
+#pragma unroll
+    for (int i = 0; i < TJN; ++i) {
+      const int r = (wid * TJN + i) * 8 + (ln >> 3);
+      const int c = (ln & 7) ^ swz2(r);
       b_off[i] = static_cast<uint32_t>(min(n0 + r, N - 1) - n0) * static_cast<uint32_t>(K) + 16u * c;
     }
     ra = make_rsrc(xq + static_cast<int64_t>(m0) * K);
     rb = make_rsrc(wq + static_cast<int64_t>(n0) * K);
   };
-  const int wm = (wid & 1) * 128, wn = (wid >> 1) * 64;
+  const int wm = (wid & 1) * 128, wn = (wid >> 1) * (16 * TJN);
   const int rra = wm + (lane & 15), rrb = wn + (lane & 15);
   int a_rd[2], b_rd[2];
 #pragma unroll
@@ -836,40 +842,42 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
   const int ns = K / kSlice2;
   const int last = (ns - 1) * kSlice2;
   auto prologue = [&]() {
-    issue_stage2(ra, lA0, a_off, 0, wid);
-    issue_stage2(rb, lB0, b_off, 0, wid);
+    issue_rows2<kDma2PerWave>(ra, lA0, a_off, 0, wid);
+    issue_rows2<TJN>(rb, lB0, b_off, 0, wid);
     memory_opaque();
-    issue_stage2(ra, lA1, a_off, min(kSlice2, last), wid);
-    issue_stage2(rb, lB1, b_off, min(kSlice2, last), wid);
+    issue_rows2<kDma2PerWave>(ra, lA1, a_off, min(kSlice2, last), wid);
+    issue_rows2<TJN>(rb, lB1, b_off, min(kSlice2, last), wid);
   };
   int v = blockIdx.x;
   setup(v);
   prologue();
 
   for (;;) {
-    v4f acc[TI][TJ];
+    v4f acc[TI][TJN];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    __builtin_amdgcn_s_waitcnt(0x0F78);     // vmcnt(8): stage 0 landed (see k_gemm_tile)
+      for (int j = 0; j < TJN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // stage 0 landed: at most stage 1's 4 + TJN DMA instructions outstanding (see k_gemm_tile)
+    constexpr int kStageDma = kDma2PerWave + TJN;
+    __builtin_amdgcn_s_waitcnt((kStageDma & 15) | ((kStageDma >> 4) << 14) | 0x0F70);
     stage_barrier();
-    v8i fb[TJ], a_cur;
+    v8i fb[TJN], a_cur;
     {
       // in asm, as in k_gemm_tile: both K halves of the B blocks and of A block 0
-      uint32_t addr[2 * TJ + 2];
-      v4i r[2 * TJ + 2];
+      uint32_t addr[2 * TJN + 2];
+      v4i r[2 * TJN + 2];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
+      for (int j = 0; j < TJN; ++j) {
         addr[2 * j] = lds_addr(lB0) + j * 16 * kSlice2 + b_rd[0];
         addr[2 * j + 1] = lds_addr(lB0) + j * 16 * kSlice2 + b_rd[1];
       }
-      addr[2 * TJ] = lds_addr(lA0) + a_rd[0];
-      addr[2 * TJ + 1] = lds_addr(lA0) + a_rd[1];
+      addr[2 * TJN] = lds_addr(lA0) + a_rd[0];
+      addr[2 * TJN + 1] = lds_addr(lA0) + a_rd[1];
       lds_read_frags(r, addr);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) fb[j] = __builtin_shufflevector(r[2 * j], r[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      a_cur = __builtin_shufflevector(r[2 * TJ], r[2 * TJ + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int j = 0; j < TJN; ++j) fb[j] = __builtin_shufflevector(r[2 * j], r[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      a_cur = __builtin_shufflevector(r[2 * TJN], r[2 * TJN + 1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
 #define SQ_FP8_STAGE(LA, LB, LA_NXT, LB_NXT)                                                              \
@@ -878,7 +886,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
       const v8i a_nxt = lds_frag8(LA + (i + 1) * 16 * kSlice2, a_rd[0], a_rd[1]);                        \
       fp8_block(acc[i], a_cur, fb);                                                                      \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); /* the two LDS reads of block i+1 */            \
-      __builtin_amdgcn_sched_group_barrier(0x008, TJ, 0); /* then block i's MFMAs */                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, TJN, 0); /* then block i's MFMAs */                    \
       a_cur = a_nxt;                                                                                     \
     }                                                                                                    \
     fp8_block(acc[TI - 1], a_cur, fb);                                                                   \
@@ -886,9 +894,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
     __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0): stage s+1 landed, stage s reads done */ \
     stage_barrier();                                                                                     \
     const int kn = min((s + 2) * kSlice2, last);                                                          \
-    issue_stage2(ra, LA, a_off, kn, wid);                                                                \
-    issue_stage2(rb, LB, b_off, kn, wid);                                                                \
-    _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                                       \
+    issue_rows2<kDma2PerWave>(ra, LA, a_off, kn, wid);                                                   \
+    issue_rows2<TJN>(rb, LB, b_off, kn, wid);                                                            \
+    _Pragma("unroll") for (int j = 0; j < TJN; ++j)                                                      \
       fb[j] = lds_frag8(LB_NXT + j * 16 * kSlice2, b_rd[0], b_rd[1]);                                    \
     a_cur = lds_frag8(LA_NXT, a_rd[0], a_rd[1]);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                                   \
@@ -905,11 +913,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
 
     // this tile's scales before the next tile's DMAs, then the epilogue (as k_gemm_tile)
     const int cm0 = m0, cn0 = n0;
-    float xsv[TI], wv[TJ][4];
+    float xsv[TI], wv[TJN][4];
 #pragma unroll
     for (int i = 0; i < TI; ++i) xsv[i] = xs[min(cm0 + wm + 16 * i + (lane & 15), M - 1)];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+    for (int j = 0; j < TJN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) wv[j][r] = ws[min(cn0 + wn + 16 * j + 4 * (lane >> 4) + r, N - 1)];
     stage_barrier();
@@ -924,9 +932,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
       for (int i = 0; i < TI; ++i) {
         const int m = cm0 + wm + 16 * i + (lane & 15);
 #pragma unroll
-        for (int j = 0; j < TJ; j += 2)
+        for (int j = 0; j + 1 < TJN; j += 2)
           store8_pair<YDT, v4f>(y, M, N, m, cn0 + wn + 16 * j, acc[i][j], acc[i][j + 1], xsv[i], wv[j], wv[j + 1],
                                 bias, lane);
+        if constexpr (TJN % 2 == 1) {                   // the odd last tile, four outputs per lane
+          const int n = cn0 + wn + 16 * (TJN - 1) + 4 * (lane >> 4);
+          if (m < M && n < N) store4_pre<YDT, v4f>(y, N, m, n, acc[i][TJN - 1], xsv[i], wv[TJN - 1], bias);
+        }
       }
     } else {
 #pragma unroll
@@ -934,7 +946,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
         const int m = cm0 + wm + 16 * i + (lane & 15);
         if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
+        for (int j = 0; j < TJN; ++j) {
           const int n = cn0 + wn + 16 * j + 4 * (lane >> 4);
           if (n < N) store4_pre<YDT, v4f>(y, N, m, n, acc[i][j], xsv[i], wv[j], bias);
         }
@@ -1513,18 +1525,28 @@ hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
 
 }  // namespace
 
+template <int YDT, int TJN>
+hipError_t launch_tile_fp8(const GemmArgs& g, int tiles_m, int group, hipStream_t st) {
+  const int tiles_n = (g.N + 64 * TJN - 1) / (64 * TJN);
+  int grid = 0;
+  if (hipError_t e = tile_grid(reinterpret_cast<const void*>(k_gemm_tile_fp8<YDT, TJN>), tiles_m * tiles_n, &grid))
+    return e;
+  hipLaunchKernelGGL((k_gemm_tile_fp8<YDT, TJN>), dim3(grid), dim3(512), 0, st,
+                     reinterpret_cast<const uint8_t*>(g.xq), g.x_scale, reinterpret_cast<const uint8_t*>(g.wq),
+                     g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
+  return hipGetLastError();
+}
+
 template <int YDT>
 hipError_t launch_fp8_typed(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 64) return launch_decode<YDT, true>(g, st);
   const int tiles_m = (g.M + kTile - 1) / kTile;
-  const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
-  int grid = 0;
-  if (hipError_t e = tile_grid(reinterpret_cast<const void*>(k_gemm_tile_fp8<YDT>), tiles_m * tiles_n, &grid)) return e;
-  hipLaunchKernelGGL((k_gemm_tile_fp8<YDT>), dim3(grid), dim3(512), 0, st,
-                     reinterpret_cast<const uint8_t*>(g.xq), g.x_scale, reinterpret_cast<const uint8_t*>(g.wq),
-                     g.w_scale, g.bias, g.y, g.M, g.N, g.K, tiles_m, tiles_n, group);
-  return hipGetLastError();
+  int tjn = 4;
+  if (hipError_t e = tile_width(g.M, g.N, &tjn)) return e;
+  if (tjn == 3) return launch_tile_fp8<YDT, 3>(g, tiles_m, group, st);
+  if (tjn == 2) return launch_tile_fp8<YDT, 2>(g, tiles_m, group, st);
+  return launch_tile_fp8<YDT, 4>(g, tiles_m, group, st);
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
