@@ -249,6 +249,32 @@ def test_gemm_persistent_grid_accumulators(mnk):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
 
 
+# Seeded random prefill shapes: every tile width (the launch picks 256, 192 or 128 columns from the
+# grid), both stage kernels (K % 128 == 0 and 64), ragged edges, one to several tiles per workgroup.
+# One random row per 256-row tile-row and the edge rows, against all columns.
+def _random_gemm_shapes(count=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        m, n, k = int(rng.integers(65, 3000)), int(rng.integers(1, 24000)), int(rng.integers(1, 48)) * 64
+        if m * n * k <= 6e10:
+            out.append((m, n, k))
+    return out
+
+
+@pytest.mark.parametrize("mnk", _random_gemm_shapes(), ids=lambda s: "x".join(map(str, s)))
+def test_gemm_random_prefill_shapes(mnk):
+    m, n, k = mnk
+    xq, wq = rand_int8((m, k), 1000 + m), rand_int8((n, k), 2000 + n)
+    acc = sq.sq_w8a8_gemm(cuda(xq), None, cuda(wq), None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(m * n + k)
+    rows = np.unique(np.r_[np.minimum(np.arange(0, m, 256) + rng.integers(0, 256, -(-m // 256)), m - 1), [0, m - 1]])
+    ref = O.int_gemm(xq.numpy()[rows], wq.numpy())
+    got = host(acc)[rows].astype(np.int64)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} accumulators differ"
+
+
 @pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("mnk", [(2100, 8000, 256), (1281, 10760, 256)], ids=lambda s: "x".join(map(str, s)))
 def test_gemm_persistent_grid_dequant_with_bias(out, mnk):
