@@ -116,15 +116,36 @@ class ClockSampler:
     marked '*' holds the current clock, which the driver updates continuously) from a host thread
     every ~2 ms while a workload runs: a same-run measure of the clock the GEMM holds. (The
     gpu-metrics table behind amdsmi refreshes only every few hundred ms on this driver, so it is
-    not used.)"""
+    not used.) Where the card's hwmon directory has them, the board power (power1_input, or
+    power1_average; microwatts) is sampled in the same loop and the power cap (power1_cap) read once."""
 
-    def __init__(self, path=None):
+    def __init__(self, path=None, hwmon=None):
         import glob
         paths = [path] if path else sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
         if len(paths) != 1:
             raise RuntimeError(f"expected one pp_dpm_sclk, found {paths}")
         self.path = paths[0]
         self.samples = []
+        self.watts = []
+        dirs = [hwmon] if hwmon else sorted(glob.glob(os.path.join(os.path.dirname(self.path), "hwmon", "hwmon*")))
+        self.power_path = self.cap_path = None
+        for d in dirs[:1]:
+            for name in ("power1_input", "power1_average"):
+                if os.path.exists(os.path.join(d, name)):
+                    self.power_path = os.path.join(d, name)
+                    break
+            if os.path.exists(os.path.join(d, "power1_cap")):
+                self.cap_path = os.path.join(d, "power1_cap")
+
+    def read_watts(self):
+        with open(self.power_path) as f:
+            return int(f.read().strip()) / 1e6
+
+    def cap_watts(self):
+        if not self.cap_path:
+            return None
+        with open(self.cap_path) as f:
+            return int(f.read().strip()) / 1e6
 
     def read_mhz(self):
         with open(self.path) as f:
@@ -144,11 +165,17 @@ class ClockSampler:
                     self.samples.append(self.read_mhz())
                 except Exception:          # a failed read is skipped, not invented
                     pass
+                if self.power_path:
+                    try:
+                        self.watts.append(self.read_watts())
+                    except Exception:
+                        pass
                 time.sleep(0.002)
         th = threading.Thread(target=loop, daemon=True)
         fn()
         torch.cuda.synchronize()
         self.samples.clear()
+        self.watts.clear()
         th.start()
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
@@ -1275,6 +1302,11 @@ def main():
                      "samples": len(mhz), "median_GHz": round(mhz[len(mhz) // 2] / 1e3, 3) if mhz else None,
                      "min_GHz": round(mhz[0] / 1e3, 3) if mhz else None,
                      "max_GHz": round(mhz[-1] / 1e3, 3) if mhz else None}
+            w = sorted(sampler.watts)
+            if w:
+                clock["board_power_W"] = {"source": f"sysfs hwmon {os.path.basename(sampler.power_path)}, same loop",
+                                          "samples": len(w), "median": round(w[len(w) // 2], 1),
+                                          "max": round(w[-1], 1), "cap": sampler.cap_watts()}
         except Exception as e:        # no clock reading on this host: say so
             clock = {"error": f"{type(e).__name__}: {e}"}
     del sites

@@ -132,3 +132,19 @@ def test_clock_sampler_reads_the_current_dpm_level(tmp_path):
     f.write_text("0: 500Mhz\n1: 573Mhz\n2: 2400Mhz\n")
     with pytest.raises(RuntimeError):
         bench.ClockSampler(str(f)).read_mhz()
+
+
+def test_clock_sampler_reads_board_power_and_cap(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1788Mhz *\n")
+    hw = tmp_path / "hwmon" / "hwmon3"
+    hw.mkdir(parents=True)
+    (hw / "power1_input").write_text("1350000000\n")
+    (hw / "power1_cap").write_text("1400000000\n")
+    s = bench.ClockSampler(str(f))
+    assert s.power_path == str(hw / "power1_input")
+    assert s.read_watts() == 1350.0 and s.cap_watts() == 1400.0
+    (hw / "power1_input").unlink()
+    (hw / "power1_average").write_text("900000000\n")
+    assert bench.ClockSampler(str(f)).read_watts() == 900.0
+    assert bench.ClockSampler(str(tmp_path / "pp_dpm_sclk"), hwmon=str(tmp_path / "none")).power_path is None
