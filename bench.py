@@ -597,7 +597,7 @@ def prefill_sweep():
         return best
 
     g = torch.Generator(device="cpu").manual_seed(1)
-    for wl_name, site_name, m, n, k in prefill_shapes():       # decode shapes (M <= 64): --decode-sweep
+    for wl_name, site_name, m, n, k in prefill_shapes():       # decode shapes: --decode-sweep
         xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, generator=g).cuda()
         wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, generator=g).cuda()
         xs = torch.rand(m, generator=g).cuda()

@@ -263,7 +263,7 @@ sq_status smoothquant_fold_fp8(const float* act_absmax, const void* w, sq_dtype 
  *   are truncated toward zero), and the group sums accumulate in binary32. So
  *   |acc - exact| <= sum_k (|p_k| mod 2^(E_g - 13)) + (K/8 + 3) 2^-24 sum_k |p_k|.
  *   The order is fixed for a given shape (results repeat bit for bit), but
- *   decode shapes (M <= 64) and larger M sum in different orders.
+ *   decode shapes (M <= 128) and larger M sum in different orders.
  *   y_dt in {F32, F16, BF16} (no raw I32 mode); K % 128 == 0 in addition to
  *   the shared limits (SQ_ERR_BAD_SHAPE otherwise).
  */

@@ -188,9 +188,9 @@ def test_fp8_mfma_group_truncation():
 
 GEMM_SHAPES = [(17, 33, 128), (256, 256, 128), (300, 520, 384), (513, 700, 1280), (64, 16416, 2176),
                (1024, 2048, 20480), (5, 9, 133120),
-               # decode (M <= 64): every token-tile count, narrow and 144-channel strips, ragged N
+               # decode (M <= 128): every token-tile count, narrow and 144-channel strips, ragged N
                (1, 9216, 9216), (2, 1000, 1280), (4, 36864, 9216), (16, 130, 384), (33, 4000, 2048),
-               (48, 16400, 1024), (64, 36864, 9216), (65, 300, 256),
+               (48, 16400, 1024), (64, 36864, 9216), (65, 300, 256), (128, 36864, 2048), (129, 300, 256),
                # N not a multiple of 4: the epilogue's partial stores, prefill and decode
                (130, 45, 256), (300, 1001, 384), (40, 37, 640)]
 
@@ -212,9 +212,10 @@ def test_fp8_gemm_accumulator(shape):
     assert np.all(err <= tol), f"max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3g}"
 
 
-# Every token count the FP8 decode kernel serves (1..64) and so every wave grid it picks, on a ragged
-# narrow strip and on the 144-channel strips, three 128-byte segments.
-@pytest.mark.parametrize("m", list(range(1, 65)))
+# Every token count the FP8 decode kernel serves up to 64 and a spread of 65-128 (eight token tiles),
+# and so every wave grid it picks, on a ragged narrow strip and on the 144-channel strips, three
+# 128-byte segments.
+@pytest.mark.parametrize("m", list(range(1, 65)) + [65, 80, 96, 127, 128])
 @pytest.mark.parametrize("n", [300, 16400])
 def test_fp8_gemm_decode_every_token_count(m, n):
     k = 384

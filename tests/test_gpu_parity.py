@@ -182,6 +182,8 @@ GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 
                (5, 36, 1984),
                # decode kernel, 144-channel strips (N >= 16384): ragged last strip, K tails
                (33, 16400, 320), (20, 16384, 1088), (64, 16416, 2112), (12, 16400, 704), (9, 300, 1216),
+               # eight token tiles (65-128 tokens) on both strip widths, K tails; 129 takes the prefill tile
+               (100, 9216, 9216), (128, 36864, 2112), (77, 16400, 1216), (129, 520, 640),
                # up to 4 tokens: the MFMA decode kernel below N = 16384, the GEMV from there; K tails inside a
                # 256-byte segment, ragged N
                (3, 130, 320), (4, 16400, 1216), (2, 77, 704), (1, 1000, 4160),
@@ -206,10 +208,13 @@ def test_gemm_i32_exact(mnk):
 
 
 # The decode kernel picks its wave grid (token groups x channel groups) from the token-tile count and
-# the strip width: every token count up to 64, on a ragged narrow strip (the MFMA kernel throughout)
-# and on the 144-channel strips (the GEMV up to 4 tokens), with an odd number of 64-byte K steps (the
-# last segment's second half is the next row's bytes).
-@pytest.mark.parametrize("m", list(range(1, 65)))
+# the strip width: every token count up to 64 and a spread of 65-128 (eight token tiles), on a ragged
+# narrow strip (the MFMA kernel throughout) and on the 144-channel strips (the GEMV up to 4 tokens),
+# with an odd number of 64-byte K steps (the last segment's second half is the next row's bytes).
+DECODE_MS = list(range(1, 65)) + [65, 72, 80, 96, 111, 112, 127, 128]
+
+
+@pytest.mark.parametrize("m", DECODE_MS)
 @pytest.mark.parametrize("nk", [(300, 192), (16400, 320)], ids=lambda s: "x".join(map(str, s)))
 def test_gemm_decode_every_token_count(m, nk):
     n, k = nk

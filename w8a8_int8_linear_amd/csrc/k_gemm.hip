@@ -17,7 +17,7 @@
 //    with 64-byte slices in a 4-stage ring, for K % 128 == 64, one tile per
 //    workgroup.
 //  * k_gemv (up to 4 tokens at N >= 16384, vector ALUs) and k_gemm_decode
-//    (the other shapes up to 64 tokens, MFMA) -- decode shapes, bound by
+//    (the other shapes up to 128 tokens, MFMA) -- decode shapes, bound by
 //    streaming wq from HBM (described at the kernels).
 //
 // MFMA operand order: the A operand (rows = lane % 16) carries 16 rows of wq and
@@ -959,12 +959,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tile_fp8(const uint8_t* __restr
 
 // ----------------------------------------------------------------------------- decode helpers
 
-// Decode shapes (M <= 64) are bound by streaming wq once from HBM. HBM and the
+// Decode shapes (M <= 128) are bound by streaming wq once from HBM. HBM and the
 // L2 serve a wave's load best when it covers whole 128-byte lines: a load in
 // the MFMA register layout (16 rows x 64 bytes) reaches about 2/3 of the rate
 // of one that covers 4 or 8 rows x 256 or 128 bytes, so the decode kernels
 // never load weights in the MFMA layout directly.
 constexpr int kDecWaves = 4;
+// Up to this many tokens the weight-streaming kernels run the GEMM. From 65 to
+// 128 tokens the 256-row prefill tile would leave half of every tile and most
+// CUs idle (36-144 tiles at N = 4096-36864): measured at K = 9216 with rotating
+// weights, eight token tiles per strip took 33-36 us against 72-74 us at
+// N = 4096 and 9216, and 82-88 against 105-110 us at N = 36864.
+constexpr int kDecMaxTokens = 128;
 // Buffer-load cache policy for the decode weight stream, read exactly once:
 // non-temporal. Measured on the 1-token GEMV, N = 36864: 6.5 against 5.8 TB/s.
 constexpr int kStreamPolicy = 2;
@@ -1399,7 +1405,7 @@ hipError_t launch_rows(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Decode shapes (M <= 64). INT8 with 1-2 tokens, K <= 9216 and N < 16384: the
+// Decode shapes (M <= 128). INT8 with 1-2 tokens, K <= 9216 and N < 16384: the
 // row GEMV (k_gemv_rows, 15.2-15.6 us at N = 9216 against 15.9-16.3 for the
 // MFMA kernel; at N = 36864 it trails k_gemv by 1-2%; with 4 tokens, 234
 // VGPRs, it took 16.6 us against the MFMA kernel's 16.0). INT8 with up to 4
@@ -1442,6 +1448,10 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
   if (mt == 3) {
     if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT, FP8>), 144)
     SQ_DECODE((k_gemm_decode<3, 3, 5, YDT, FP8>), 48)
+  }
+  if (mt > 4) {                    // 65-128 tokens: eight token tiles, one ring stage fewer to fit LDS
+    if (wide) SQ_DECODE((k_gemm_decode<9, 8, 4, YDT, FP8>), 144)
+    SQ_DECODE((k_gemm_decode<3, 8, 6, YDT, FP8>), 48)
   }
   if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT, FP8>), 144)
   SQ_DECODE((k_gemm_decode<3, 4, 5, YDT, FP8>), 48)
@@ -1507,7 +1517,7 @@ hipError_t launch_tile(const GemmArgs& g, int tiles_m, int group, hipStream_t st
 
 template <int YDT>
 hipError_t launch_typed(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64) return launch_decode<YDT, false>(g, st);
+  if (g.M <= kDecMaxTokens) return launch_decode<YDT, false>(g, st);
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int tiles_n = (g.N + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
@@ -1539,7 +1549,7 @@ hipError_t launch_tile_fp8(const GemmArgs& g, int tiles_m, int group, hipStream_
 
 template <int YDT>
 hipError_t launch_fp8_typed(const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 64) return launch_decode<YDT, true>(g, st);
+  if (g.M <= kDecMaxTokens) return launch_decode<YDT, true>(g, st);
   const int tiles_m = (g.M + kTile - 1) / kTile;
   const int group = min(tiles_m, 8);
   int tjn = 4;
