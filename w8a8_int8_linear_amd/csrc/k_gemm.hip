@@ -463,23 +463,6 @@ constexpr int kDma2PerWave = kStage2Bytes / 1024 / 8;   // DMA instructions (8 r
 // slot offsets 0, 2, 4, 6 and the 32 lanes hit 32 distinct slots.
 __device__ __forceinline__ int swz2(int r) { return ((r >> 2) & 3) << 1; }
 
-__device__ __forceinline__ void issue_stage2(__amdgpu_buffer_rsrc_t rsrc, int8_t* lds,
-                                             const uint32_t (&off)[kDma2PerWave], int k0, int wid) {
-#pragma unroll
-  for (int i = 0; i < kDma2PerWave; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + (wid * kDma2PerWave + i) * 1024), 16, off[i], k0,
-                                             0, 0);
-}
-
-// Fragments of K step t (0 or 1) of a stage.
-__device__ __forceinline__ void read_frags2(const int8_t* la, const int8_t* lb, const int (&a_rd)[2],
-                                            const int (&b_rd)[2], int t, Frags& f) {
-#pragma unroll
-  for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const v4i*>(la + a_rd[t] + i * 16 * kSlice2);
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) f.b[j] = *reinterpret_cast<const v4i*>(lb + b_rd[t] + j * 16 * kSlice2);
-}
-
 // As interleave_reads_with_mfma; on the step that refills a stage, its eight
 // DMA instructions go out two at a time between the first MFMAs.
 __device__ __forceinline__ void interleave2(bool with_dma) {

@@ -63,12 +63,6 @@ template <> __device__ __forceinline__ void raw_load<f32_t>(const void* p, Raw8<
   r.b = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + 1));
 }
 
-// 8 int8 codes (two packed words) to p (8-byte aligned), non-temporal: the
-// codes are written once and read by a later kernel.
-__device__ __forceinline__ void store_codes8(int8_t* p, uint2 w) {
-  __builtin_nontemporal_store(u32x2_t{w.x, w.y}, reinterpret_cast<u32x2_t*>(p));
-}
-
 // Rows through buffer resources: one resource per row (its base and size are
 // workgroup-uniform, so they live in scalar registers and cost no vector
 // instructions per row), and each thread's byte offsets within a row stay the
@@ -86,6 +80,8 @@ __device__ __forceinline__ void raw_load_buf<f32_t>(__amdgpu_buffer_rsrc_t r, ui
   v.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNonTemporal));
   v.b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kBufNonTemporal));
 }
+// 8 int8 codes (two packed words) at byte offset off, non-temporal: the codes
+// are written once and read by a later kernel.
 __device__ __forceinline__ void store_codes8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 w) {
   __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w.x, w.y}, r, off, 0, kBufNonTemporal);
 }
