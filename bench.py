@@ -202,19 +202,25 @@ def recorded_traffic():
 N_XCD, N_CU, SIMD_PER_CU, PEAK_SCLK_GHZ = 8, 256, 4, 2.4     # MI355X; the dense peaks are quoted at 2.4 GHz
 
 
+def _read_csv(path):
+    """Rows of a rocprofv3 CSV as dicts, the file closed on return."""
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
 def gemm_clock(clock_dir):
     """Shader clock and MFMA-busy fraction of each GEMM dispatch of a --pmc GRBM_GUI_ACTIVE
     SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES run: GRBM_GUI_ACTIVE sums the busy cycles of the
     XCDs, so cycles per XCD over the dispatch's duration is the clock; the MFMA busy cycles,
     summed over the CUs, are divided by the cycles of every SIMD."""
-    import csv
     import glob
     from collections import defaultdict
     hits = glob.glob(os.path.join(clock_dir, "**", "*counter_collection.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no counter collection under {clock_dir}")
     per = defaultdict(dict)
-    for r in csv.DictReader(open(hits[0])):
+    for r in _read_csv(hits[0]):
         if "k_gemm_tile" in r["Kernel_Name"]:
             d = per[int(r["Dispatch_Id"])]
             d[r["Counter_Name"]] = float(r["Counter_Value"])
@@ -235,7 +241,6 @@ def summarize_counters(trace_dir, fetch_dir, write_dir, clock_dir=None):
     With clock_dir (a GRBM_GUI_ACTIVE / MFMA-busy run), the record also carries each GEMM
     dispatch's shader clock and MFMA-busy fraction.
     """
-    import csv
     import glob
     from collections import defaultdict
 
@@ -245,10 +250,10 @@ def summarize_counters(trace_dir, fetch_dir, write_dir, clock_dir=None):
             raise SystemExit(f"no {pat} under {d}")
         return hits[0]
 
-    stats = list(csv.DictReader(open(one(trace_dir, "*kernel_stats.csv"))))
+    stats = list(_read_csv(one(trace_dir, "*kernel_stats.csv")))
     counters = {}
     for name, d in [("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)]:
-        rows = [r for r in csv.DictReader(open(one(d, "*counter_collection.csv"))) if r["Counter_Name"] == name]
+        rows = [r for r in _read_csv(one(d, "*counter_collection.csv")) if r["Counter_Name"] == name]
         copy = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
         copy = max(copy, key=lambda r: float(r["Counter_Value"]))
         per = defaultdict(list)
@@ -453,7 +458,6 @@ def summarize_decode_counters(pmc_dir):
     shares of wave cycles spent waiting on LDS instructions and issuing them, summed over the
     instance's dispatches (SQ_LDS_BANK_CONFLICT counts the LDS unit's stall cycles, not wave
     cycles, so it is not turned into a share)."""
-    import csv
     import glob
     from collections import defaultdict
     hits = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -461,7 +465,7 @@ def summarize_decode_counters(pmc_dir):
         raise SystemExit(f"no counter collection under {pmc_dir}")
     tot = defaultdict(lambda: defaultdict(float))
     calls = defaultdict(set)
-    for r in csv.DictReader(open(hits[0])):
+    for r in _read_csv(hits[0]):
         name = r["Kernel_Name"]
         if "sq::k_gemm_decode" not in name and "sq::k_gemv" not in name:
             continue
@@ -495,14 +499,13 @@ def summarize_ln_counters(pmc_dir, m=8192, k=20480):
     the XCDs. Lane instructions per element = 64 x instructions / (M K); a CU issues at most one VALU
     wave instruction per cycle (four SIMDs, four cycles each), so the issue share is instructions over
     CU cycles."""
-    import csv
     import glob
     from collections import defaultdict
     hits = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no counter collection under {pmc_dir}")
     per = defaultdict(dict)
-    for r in csv.DictReader(open(hits[0])):
+    for r in _read_csv(hits[0]):
         if "sq::k_norm_quant<sq::f16_t, 1," in r["Kernel_Name"]:
             d = per[int(r["Dispatch_Id"])]
             d[r["Counter_Name"]] = float(r["Counter_Value"])
@@ -530,12 +533,11 @@ def summarize_ln_counters(pmc_dir, m=8192, k=20480):
 def summarize_decode(trace_dir, fp8=False):
     """Kernel durations of a --decode-sweep trace (with --fp8: of --decode-sweep --fp8), matched to
     its shapes by dispatch order."""
-    import csv
     import glob
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no kernel trace under {trace_dir}")
-    rows = [r for r in csv.DictReader(open(hits[0])) if "sq::" in r["Kernel_Name"]]
+    rows = [r for r in _read_csv(hits[0]) if "sq::" in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     per = DEC_WARM + DEC_ITERS
     shapes = [(m, n) for n in DEC_NS for m in DEC_MS]
@@ -631,13 +633,12 @@ def summarize_prefill(trace_dir):
     """Per-shape durations of this library's GEMM in a --prefill-sweep kernel trace. Dispatches are
     taken in start order; each shape's launches are the next PREFILL_WARM + PREFILL_TIMES * reps
     GEMM dispatches."""
-    import csv
     import glob
     import statistics
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no kernel trace under {trace_dir}")
-    rows = sorted((r for r in csv.DictReader(open(hits[0])) if "sq::k_gemm" in r["Kernel_Name"]),
+    rows = sorted((r for r in _read_csv(hits[0]) if "sq::k_gemm" in r["Kernel_Name"]),
                   key=lambda r: int(r["Start_Timestamp"]))
     shapes = prefill_shapes()
     counts = [PREFILL_WARM + PREFILL_TIMES * prefill_reps(m, n, k) for _, _, m, n, k in shapes]
@@ -740,7 +741,6 @@ def granularity_sweep(args):
 
 def kernel_stats_table(trace_dir, title, cmd, flag, note, out_name):
     """A rocprofv3 --kernel-trace --stats run's per-kernel statistics as a profiles/ table."""
-    import csv
     import glob
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not hits:
@@ -748,7 +748,7 @@ def kernel_stats_table(trace_dir, title, cmd, flag, note, out_name):
     lines = [f"# rocprofv3 kernel statistics: {title}", "",
              f"Command: `{cmd}`, then `python bench.py {flag} <dir>`.", "", note, "",
              "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
-    for r in csv.DictReader(open(hits[0])):
+    for r in _read_csv(hits[0]):
         if "sq::" in r["Name"]:
             short = r["Name"].split("(")[0].replace("void ", "")
             lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
@@ -890,7 +890,8 @@ def summarize_llm_int8(trace_dir, sweep_log=None):
         "quantisation) appear too; each kernel's row mixes every site it ran on.",
         "llm_int8_vs_smoothquant.md")
     if sweep_log:
-        recs = [json.loads(ln) for ln in open(sweep_log) if ln.startswith("{")]
+        with open(sweep_log) as f:
+            recs = [json.loads(ln) for ln in f if ln.startswith("{")]
         lines = ["", "Per site, HIP-event medians of whole calls in the same run (the profiler's overhead included):",
                  "", "| workload | site | M x N x K | outlier channels | SmoothQuant ms | LLM.int8() ms | ratio |",
                  "|---|---|---|---|---|---|---|"]
@@ -906,14 +907,13 @@ def summarize_llm_int8(trace_dir, sweep_log=None):
 def summarize_fp8(trace_dir):
     """Per-dispatch durations of a --fp8 kernel trace, grouped by kernel and grid (one kernel name
     serves both the activation quantiser and the fold's weight quantiser), as a profiles/ table."""
-    import csv
     import glob
     import statistics
     hits = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not hits:
         raise SystemExit(f"no kernel trace under {trace_dir}")
     groups = {}
-    for r in csv.DictReader(open(hits[0])):
+    for r in _read_csv(hits[0]):
         if "sq::" not in r["Kernel_Name"]:
             continue
         short = r["Kernel_Name"].split("(")[0].replace("void ", "")

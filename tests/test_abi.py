@@ -16,7 +16,8 @@ A4 = ctypes.c_void_p((1 << 20) + 4)   # 4-byte aligned, not 16-byte aligned
 
 
 def _declared():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     return set(re.findall(r"^(?:sq_status|const char\*)\s+(\w+)\s*\(", text, re.M))
 
 
