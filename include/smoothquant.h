@@ -32,11 +32,12 @@
  *    looked up once under a lock.
  *
  * Number format readings (the pages state none of them): an INT8 step is
- * fl32(absmax / 127) with IEEE division, codes are round-half-to-even of
- * fl32(v / step) clipped to [-127, 127], and a zero step gives zero codes. Norm
- * statistics are taken in binary64 and rounded once to binary32. The _fp8 calls
- * use OCP E4M3 codes (uint8) with steps fl32(absmax / 448), round half to even,
- * and saturate to +-448 where a step is given for a whole tensor.
+ * fl32(absmax / 127), the correctly rounded quotient; codes are
+ * round-half-to-even of fl32(v / step) clipped to [-127, 127], and a zero
+ * step gives zero codes. Norm statistics are taken in binary64 and rounded
+ * once to binary32. The _fp8 calls use OCP E4M3 codes (uint8) with steps
+ * fl32(absmax / 448), round half to even, and saturate to +-448 where a step
+ * is given for a whole tensor.
  */
 #ifndef SMOOTHQUANT_H_
 #define SMOOTHQUANT_H_

@@ -151,9 +151,11 @@ __device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
 // of the row; every step combines two equal-sized partial results in an order
 // that is the same on both lanes, so all 16 lanes end with identical bits. The
 // four row results are then combined in a fixed order from uniform values.
+// (Every lane's source exists for these patterns, so no lane keeps an old
+// value: the move needs no initialised destination.)
 template <int CTRL>
 __device__ __forceinline__ int dpp_move(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_move(double v) {
@@ -262,19 +264,34 @@ __device__ __forceinline__ float block_max(float v, float* red) {   // v >= 0
 }
 
 // ----------------------------------------------------------------------------- INT8 codes
-// Step of a row: fl32(absmax / 127) with IEEE division.
-__device__ __forceinline__ float int8_step(float amax) { return div_rn(amax, 127.0f); }
+// Step of a row: fl32(absmax / 127), as fl32(fl64(absmax * fl64(1/127))).
+// The binary64 value is within 2^-51 relative of q = absmax / 127, while q
+// lies at least 2^-34 relative from every binary32 rounding boundary m near
+// it: m is an odd multiple of half a binary32 spacing h of q's binade, and
+// absmax, whose binade is 2^6 or 2^7 times higher (or, for a subnormal q, a
+// multiple of the same fixed spacing), is an even multiple of h, so
+// absmax - 127 m is a nonzero multiple of h and |q - m| >= h / 127. Both
+// therefore round to the same binary32 value.
+__device__ __forceinline__ float int8_step(float amax) {
+  return static_cast<float>(static_cast<double>(amax) * (1.0 / 127.0));
+}
 
 // Per-row quantiser: code = clip(rne(fl32(y / step)), -127, 127).
 //
 // The quotient fl32(y / step) is needed only to decide which side of a
-// half-integer it falls on. t = fl32(y * fl32(1 / step)) differs from the
-// exact quotient Q by at most |Q| * 2^-22.9 and fl32(Q) by less than
-// |Q| * 2^-22 <= 2^-15 (|Q| <= 128), so rne(t) = rne(fl32(Q)) whenever t lies
-// farther than 2^-15 from every half-integer. The rare elements inside that
-// band take the IEEE division. Steps below 2^-100 (where 1/step may overflow)
-// always divide.
+// half-integer it falls on. The exact product P = y * fl32(1 / step) differs
+// from the exact quotient Q by at most |Q| 2^-24, and fl32(Q) from Q by at
+// most |Q| 2^-24, so for |Q| <= 128 fl32(Q) lies within 2^-16 of P: rne(P)
+// = rne(fl32(Q)) whenever P lies farther than 2^-16 from every half-integer.
+// One FMA gives s = fl(P + 1.5 * 2^23), which is 1.5 * 2^23 + rne(P) for
+// |P| < 2^22 (the binary32 spacing there is 1, ties to even, and 1.5 * 2^23
+// is even), so the low byte of s's bits is rne(P) in two's complement; a
+// second FMA gives the residual d = fl(P - rne(P)) (one rounding of a value
+// below 1/2, within 2^-25). Elements with |d| >= 1/2 - 2^-15 (P within about
+// 2^-15 of a half-integer) take the IEEE division. Steps below 2^-100 (where
+// 1/step may overflow) always divide.
 struct Quantizer {
+  static constexpr float kMagic = 12582912.0f;         // 1.5 * 2^23
   float step, rcp;
   bool zero, exact_only;
   __device__ __forceinline__ explicit Quantizer(float st) : step(st) {
@@ -283,35 +300,37 @@ struct Quantizer {
     rcp = zero ? 0.0f : div_rn(1.0f, st);
   }
   // Codes of 8 values, packed little-endian into two 32-bit words. With the
-  // row's own step |t| <= amax * fl32(1/step) < 127.5 on the fast path, so
-  // rne(t) needs no clamp; CLIP (a step given for a whole tensor, which values
-  // may exceed) clamps it. The exact path always clamps (a subnormal step may
-  // push the quotient past 127). One comparison covers all 8 elements: the
-  // largest |t - rne(t)|. (NaN and Inf inputs are outside the contract; such
-  // elements get some code.)
+  // row's own step |P| <= amax * fl32(1/step) < 127.5, so rne(P) needs no
+  // clamp; CLIP (a step given for a whole tensor, which values may exceed)
+  // clamps s to 1.5 * 2^23 +- 127. For |P| >= 2^22 s is no longer
+  // 1.5 * 2^23 + rne(P), but it stays on P's side of that range, so the clamp
+  // still gives +-127 (a product that overflows fails the residual test and
+  // divides). The exact path always clamps (a subnormal step may push the
+  // quotient past 127). One comparison covers all 8 elements: the largest
+  // |d|. (NaN and Inf inputs are outside the contract; such elements get
+  // some code.)
   template <bool CLIP = false>
   __device__ __forceinline__ uint2 codes8(const float y[8]) const {
     if (zero) return make_uint2(0u, 0u);                 // workgroup-uniform
-    float q[8], d[8];
+    float m[8], d[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float t = mul_rn(y[i], rcp);
-      q[i] = rintf(t);
-      d[i] = sub_rn(t, q[i]);
+      m[i] = __builtin_fmaf(y[i], rcp, kMagic);
+      d[i] = __builtin_fmaf(y[i], rcp, kMagic - m[i]);  // kMagic - m[i] = -rne(P), exact
     }
     float dm = fabsf(d[0]);
 #pragma unroll
     for (int i = 1; i < 8; ++i) dm = fmaxf(dm, fabsf(d[i]));
     if (exact_only || !(dm < 0.499969482421875f)) {     // 0.5 - 2^-15
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(rintf(div_rn(y[i], step)), -127.0f), 127.0f);
+      for (int i = 0; i < 8; ++i) m[i] = kMagic + fminf(fmaxf(rintf(div_rn(y[i], step)), -127.0f), 127.0f);
     } else if constexpr (CLIP) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -127.0f), 127.0f);
+      for (int i = 0; i < 8; ++i) m[i] = fminf(fmaxf(m[i], kMagic - 127.0f), kMagic + 127.0f);
     }
-    int c[8];
+    uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(q[i]);
+    for (int i = 0; i < 8; ++i) c[i] = __float_as_uint(m[i]);
     // low bytes: perm(hi, lo, sel) picks bytes of {hi:lo}; 0x0c gives 0x00
     const uint32_t w0 = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u) | __builtin_amdgcn_perm(c[3], c[2], 0x04000c0cu);
     const uint32_t w1 = __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u) | __builtin_amdgcn_perm(c[7], c[6], 0x04000c0cu);
