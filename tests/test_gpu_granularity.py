@@ -93,6 +93,43 @@ def test_norm_quant_static(dtype, norm, shape, factor):
         assert (np.abs(host(xq).astype(np.int32)) == 127).sum() > 1       # clipping happened
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("factor", [1e-5, 1e-20, 2.0 ** -120])
+def test_norm_quant_static_far_below_range(dtype, factor):
+    """Static steps far below the tensor's own: quotients from the clipping edge up to far past
+    2^22 (the fast path's magic-constant range), and (2^-120) steps below 2^-100, which always
+    divide. Codes and steps bit for bit against the oracle."""
+    m, k = 33, 4096
+    x, gamma, beta = _inputs("nqf", dtype, "layernorm", m, k)
+    _, xs_dyn, _ = O.norm_quant_per_tensor(to_numpy(x), dtype, "layernorm", _np(gamma), _np(beta), 1e-5)
+    step = F32(np.float64(xs_dyn[0]) * factor)
+    assert step > 0
+    st = torch.tensor([step], dtype=torch.float32, device="cuda")
+    xq, xs = sq.sq_norm_quant_static(_cuda(x), st, "layernorm", _cuda(gamma), _cuda(beta), 1e-5)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):
+        q, xsr, info = O.norm_quant_per_tensor(to_numpy(x), dtype, "layernorm", _np(gamma), _np(beta), 1e-5, step=step)
+    _compare(q, xsr, info, host(xq), host(xs), f"{dtype}/x{factor}",
+             (to_numpy(x), dtype, "layernorm", _np(gamma), _np(beta), 1e-5))
+    assert (np.abs(host(xq).astype(np.int32)) == 127).mean() > 0.9
+
+
+def test_norm_quant_static_product_overflow():
+    """binary32 values near 1e30 with a static step of 1e-12: y * fl32(1/step) overflows binary32,
+    which must send those elements to the divide path (codes +-127, sign kept)."""
+    g = torch.Generator().manual_seed(7)
+    x = (torch.randn(5, 1024, generator=g) * 1e30).float()
+    x[0, :8] = torch.tensor([0.0, -0.0, 1e-30, -1e-30, 3e-12, -3e-12, 1e-12, 5e-13])
+    step = F32(1e-12)
+    st = torch.tensor([step], dtype=torch.float32, device="cuda")
+    xq, xs = sq.sq_norm_quant_static(_cuda(x), st, "none")
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):                     # the oracle's quotients overflow to inf, then clip
+        q, xsr, info = O.norm_quant_per_tensor(x.numpy(), "f32", "none", None, None, 1e-5, step=step)
+    assert np.array_equal(q, host(xq)) and np.array_equal(bits(xsr), bits(host(xs)))
+    assert set(np.unique(q[:, 8:])) <= {-127, 127}
+
+
 @pytest.mark.parametrize("step", [0.0, -1.0])
 def test_norm_quant_static_nonpositive_step_gives_zero_codes(step):
     x, gamma, beta = _inputs("nqz", "f16", "layernorm", 9, 4096)
