@@ -81,6 +81,32 @@ def test_norm_quant_edge_rows(dtype):
     assert q[2, :4].tolist() == [127, -4, 2, -4] and not q[0].any() and not q[1].any()
 
 
+def test_norm_quant_near_half_integers():
+    """Quotients at and around half-integers, on both sides of the quantiser's 2^-15 residual band:
+    y = fl32((n + 1/2 + d) * step) for every n in [-127, 126] and offsets d from 0 to 2^-8, under
+    a step of exactly 1 and three steps that are not powers of two. Codes and steps bit for bit."""
+    k = 1024
+    offs = [0.0] + [s * 2.0 ** e for e in (-22, -18, -16, -15.5, -15, -14.5, -14, -12, -8) for s in (1, -1)]
+    rows = []
+    for amax in (127.0, 100.0, 3.3e-3, 5.0e4):
+        step = np.float32(np.float32(amax) / np.float32(127.0))
+        vals = [np.float32((n + 0.5 + d) * np.float64(step)) for d in offs for n in range(-127, 127)]
+        row = np.zeros(len(vals) + 1, np.float32)
+        row[0] = amax
+        row[1:] = np.clip(vals, -amax, amax)
+        for start in range(0, row.size, k - 1):
+            r = np.zeros(k, np.float32)
+            r[0] = amax
+            chunk = row[1 + start:1 + start + k - 1]
+            r[1:1 + chunk.size] = chunk
+            rows.append(r)
+    x = torch.from_numpy(np.stack(rows))
+    xq, xs = sq.sq_norm_quant(cuda(x), "none", None, None, 1e-5)
+    torch.cuda.synchronize()
+    check_norm_quant(x.numpy(), "f32", "none", None, None, 1e-5, host(xq), host(xs), label="near-half")
+    assert host(xs)[0] == np.float32(1.0)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("k", [20480, 66560, 81920])
 def test_norm_quant_none_many_rows(dtype, k):
