@@ -130,6 +130,25 @@ def test_norm_quant_static_product_overflow():
     assert set(np.unique(q[:, 8:])) <= {-127, 127}
 
 
+@pytest.mark.parametrize("step", [1.5 * 2.0 ** 126, 3.0e38])
+def test_norm_quant_static_huge_step(step):
+    """A static step above 2^126, where fl32(1/step) is subnormal: quotients of binary32 values up to
+    FLT_MAX stay below 4, and half-integer quotients must still round to even."""
+    g = torch.Generator().manual_seed(11)
+    x = (torch.rand(6, 512, generator=g) * 2 - 1).double() * 3.4e38
+    st32 = np.float32(step)
+    halves = [k for k in (0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 1.0, -1.0) if abs(k) * float(st32) < 3.4e38]
+    x[0, :len(halves)] = torch.tensor(halves, dtype=torch.float64) * float(st32)   # exact in binary32
+    x = x.float()
+    assert torch.isfinite(x).all()
+    st = torch.tensor([st32], dtype=torch.float32, device="cuda")
+    xq, xs = sq.sq_norm_quant_static(_cuda(x), st, "none")
+    torch.cuda.synchronize()
+    q, xsr, info = O.norm_quant_per_tensor(x.numpy(), "f32", "none", None, None, 1e-5, step=st32)
+    assert np.array_equal(q, host(xq)) and np.array_equal(bits(xsr), bits(host(xs)))
+    assert q[0, :len(halves)].tolist() == [int(np.rint(k)) for k in halves]
+
+
 @pytest.mark.parametrize("step", [0.0, -1.0])
 def test_norm_quant_static_nonpositive_step_gives_zero_codes(step):
     x, gamma, beta = _inputs("nqz", "f16", "layernorm", 9, 4096)

@@ -289,7 +289,9 @@ __device__ __forceinline__ float int8_step(float amax) {
 // second FMA gives the residual d = fl(P - rne(P)) (one rounding of a value
 // below 1/2, within 2^-25). Elements with |d| >= 1/2 - 2^-15 (P within about
 // 2^-15 of a half-integer) take the IEEE division. Steps below 2^-100 (where
-// 1/step may overflow) always divide.
+// 1/step may overflow) always divide. (Only a step given for a whole tensor
+// can exceed 2^126, where fl32(1 / step) is subnormal and coarser; then
+// |Q| <= FLT_MAX / step < 4 and |P - Q| < 2^-21, still inside the margin.)
 struct Quantizer {
   static constexpr float kMagic = 12582912.0f;         // 1.5 * 2^23
   float step, rcp;
