@@ -213,10 +213,10 @@ def test_fp8_gemm_accumulator(shape):
 
 
 # Every token count the FP8 decode kernel serves up to 64 and a spread of 65-128 (eight token tiles),
-# and so every wave grid it picks, on a ragged narrow strip and on the 144-channel strips, three
-# 128-byte segments.
+# and so every wave grid it picks, on narrow strips (4 channels at N = 300; 40 at N = 9250, the last
+# strip 10 rows) and on the 144-channel strips, three 128-byte segments.
 @pytest.mark.parametrize("m", list(range(1, 65)) + [65, 80, 96, 127, 128])
-@pytest.mark.parametrize("n", [300, 16400])
+@pytest.mark.parametrize("n", [300, 9250, 16400])
 def test_fp8_gemm_decode_every_token_count(m, n):
     k = 384
     xq = _codes((m, k), 500 + m, 40.0)

@@ -240,8 +240,10 @@ def test_gemm_i32_exact(mnk):
 DECODE_MS = list(range(1, 65)) + [65, 72, 80, 96, 111, 112, 127, 128]
 
 
+# Below N = 16384 a decode workgroup takes N / CUs channels rounded up to a multiple of 4 (4 at
+# N = 300, 40 at N = 9250 with a 10-row last strip), the 144-channel strips above.
 @pytest.mark.parametrize("m", DECODE_MS)
-@pytest.mark.parametrize("nk", [(300, 192), (16400, 320)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("nk", [(300, 192), (9250, 256), (16400, 320)], ids=lambda s: "x".join(map(str, s)))
 def test_gemm_decode_every_token_count(m, nk):
     n, k = nk
     xq = rand_int8((m, k), 300 + m)

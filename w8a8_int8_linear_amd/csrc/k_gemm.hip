@@ -971,9 +971,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, 
 // The decode kernel with the prefill kernel's LDS layout: K in 128-byte
 // segments (two MFMA K steps), operand tiles of 16 rows x 128 bytes (row r at
 // r * 128, chunk c at slot c ^ swz2(r)), and DMA blocks of 8 rows x 128 bytes,
-// two per tile. A workgroup owns NT channel tiles (up to 9: a 144-channel
-// strip, so 36864 channels make exactly 256 workgroups and each xq segment
-// serves NT weight tiles). Every wave works on every segment, on its own
+// two per tile. A workgroup owns a strip of ch <= 16 NT channels (a multiple
+// of 4) in NT channel tiles (up to 9: a 144-channel strip, so 36864 channels
+// make exactly 256 workgroups and each xq segment serves NT weight tiles);
+// rows past the strip read zeros and are not stored. Every wave works on every segment, on its own
 // block of channel tiles x token tiles (1, 2 or 4 token groups times 4, 2 or
 // 1 channel groups, whichever leaves the busiest wave the least MFMA and LDS
 // work), and stores its own outputs: no partial sums pass between waves. Segments go
@@ -1012,7 +1013,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
                                                                 const int8_t* __restrict__ wq,
                                                                 const float* __restrict__ ws,
                                                                 const float* __restrict__ bias, void* __restrict__ y,
-                                                                int M, int N, int K) {
+                                                                int M, int N, int K, int ch) {
   static_assert(R >= 3 && R <= 8, "ring depth");
   constexpr int kTiles = NT + MT;
   constexpr int kWPer = (2 * NT + kDecWaves - 1) / kDecWaves;     // weight DMA blocks per wave per segment
@@ -1046,8 +1047,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * (16 * NT);
-  const int rows_w = min(16 * NT, N - n0);
+  const int n0 = blockIdx.x * ch;                                  // ch <= 16 NT channels, a multiple of 4
+  const int rows_w = min(ch, N - n0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc_n(wq + static_cast<int64_t>(n0) * K, static_cast<uint32_t>(rows_w * K));
   const __amdgpu_buffer_rsrc_t rx = make_rsrc_n(xq, static_cast<uint32_t>(M * K));
   const int steps = K >> 6;
@@ -1166,7 +1167,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(const int8_t* __
       if (u0 + u >= MT) continue;                                  // uniform
       const int m = 16 * (u0 + u) + (lane & 15);
       const int n = n0 + 16 * (c0 + j) + 4 * (lane >> 4);
-      if (m < M && n < N) store4<YDT>(y, N, m, n, acc[j][u], (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
+      if (m < M && n < n0 + rows_w) store4<YDT>(y, N, m, n, acc[j][u], (YDT == SQ_DT_I32) ? 0.0f : xs[m], ws, bias);
     }
   }
 }
@@ -1389,26 +1390,40 @@ hipError_t launch_rows(const GemmArgs& g, hipStream_t st) {
 }
 
 // Decode shapes (M <= 128). INT8 with 1-2 tokens, K <= 9216 and N < 16384: the
-// row GEMV (k_gemv_rows, 15.2-15.6 us at N = 9216 against 15.9-16.3 for the
+// row GEMV (k_gemv_rows, 14.7-15.6 us at N = 9216 against 15.8-16.8 for the
 // MFMA kernel; at N = 36864 it trails k_gemv by 1-2%; with 4 tokens, 234
 // VGPRs, it took 16.6 us against the MFMA kernel's 16.0). INT8 with up to 4
-// tokens at N >= 16384: the
-// vector-ALU GEMV, 16 channels per workgroup (6.8 TB/s at N = 36864, where the
-// MFMA kernel reaches 6.5). Otherwise the MFMA decode kernel (gfx950 has no
-// FP8 dot product on the vector ALUs, so FP8 always takes it) with up to 9
-// channel tiles per workgroup, so that each token segment serves many weight
-// tiles. At smaller N, 3 tiles: 48-channel strips put 192 workgroups on the
-// CUs where 64-channel strips put 144 (10-11% faster at 8-32 tokens), and at
-// N = 9216 this kernel beats the GEMV at 1-4 tokens as well (15.9-16.2
-// against 16.9-17.5 us). Measured on K = 9216, N = 9216 / 36864.
+// tokens at N >= 16384: the vector-ALU GEMV, 16 channels per workgroup (6.8
+// TB/s at N = 36864, where the MFMA kernel reaches 6.5). Otherwise the MFMA
+// decode kernel (gfx950 has no FP8 dot product on the vector ALUs, so FP8
+// always takes it) with up to 9 channel tiles per workgroup, so that each
+// token segment serves many weight tiles: 144-channel strips at N >= 16384
+// (256 workgroups at N = 36864). Below that, 3 tiles, but each workgroup
+// takes only its share of the channels, N / CUs rounded up to a multiple of 4
+// (36 at N = 9216: the third tile has 4 real rows, its other rows read zeros
+// without touching memory), so that every CU streams weights. Against 48
+// channels (192 workgroups at N = 9216) that took 4-64 tokens from 17.0-28.9
+// to 16.8-27.8 us (32 tokens: 21.7 to 19.4), and 8 tokens at N = 4096 from 8.8
+// to 8.5 us. 48-channel strips had beaten 64-channel ones (144 workgroups) by
+// 10-11% at 8-32 tokens. Measured on K = 9216, N = 9216 / 36864.
 template <int YDT, bool FP8>
 hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
   const int mt = (g.M + 15) / 16;
   const bool wide = g.N >= 16384;
+  int dev = 0, cus = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return e;
+  const int narrow = min(48, max(4, ((g.N + max(cus, 1) - 1) / max(cus, 1) + 3) & ~3));   // channels per workgroup
 #define SQ_DECODE(KERN, CH)                                                                                  \
   {                                                                                                          \
     hipLaunchKernelGGL(KERN, dim3((g.N + (CH) - 1) / (CH)), dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale,   \
-                       g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K);                                        \
+                       g.wq, g.w_scale, g.bias, g.y, g.M, g.N, g.K, (CH));                                  \
+    return hipGetLastError();                                                                                \
+  }
+#define SQ_GEMV(KERN)                                                                                        \
+  {                                                                                                          \
+    hipLaunchKernelGGL(KERN, dim3((g.N + 15) / 16), dim3(256), 0, st, g.xq, g.x_scale, g.wq, g.w_scale,     \
+                       g.bias, g.y, g.M, g.N, g.K);                                                          \
     return hipGetLastError();                                                                                \
   }
   if (!FP8 && g.M <= 2 && g.K <= 9216 && !wide) {
@@ -1416,29 +1431,30 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
     return g.M == 1 ? launch_rows<1, 9, YDT>(g, st) : launch_rows<2, 9, YDT>(g, st);
   }
   if (!FP8 && wide) {
-    if (g.M == 1) SQ_DECODE((k_gemv<1, 3, YDT>), 16)
-    if (g.M == 2) SQ_DECODE((k_gemv<2, 3, YDT>), 16)
-    if (g.M <= 4) SQ_DECODE((k_gemv<4, 2, YDT>), 16)
+    if (g.M == 1) SQ_GEMV((k_gemv<1, 3, YDT>))
+    if (g.M == 2) SQ_GEMV((k_gemv<2, 3, YDT>))
+    if (g.M <= 4) SQ_GEMV((k_gemv<4, 2, YDT>))
   }
   if (mt == 1) {
     if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT, FP8>), 144)
-    SQ_DECODE((k_gemm_decode<3, 1, 7, YDT, FP8>), 48)
+    SQ_DECODE((k_gemm_decode<3, 1, 7, YDT, FP8>), narrow)
   }
   if (mt == 2) {
     if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT, FP8>), 144)
-    SQ_DECODE((k_gemm_decode<3, 2, 6, YDT, FP8>), 48)
+    SQ_DECODE((k_gemm_decode<3, 2, 6, YDT, FP8>), narrow)
   }
   if (mt == 3) {
     if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT, FP8>), 144)
-    SQ_DECODE((k_gemm_decode<3, 3, 5, YDT, FP8>), 48)
+    SQ_DECODE((k_gemm_decode<3, 3, 5, YDT, FP8>), narrow)
   }
   if (mt > 4) {                    // 65-128 tokens: eight token tiles, one ring stage fewer to fit LDS
     if (wide) SQ_DECODE((k_gemm_decode<9, 8, 4, YDT, FP8>), 144)
-    SQ_DECODE((k_gemm_decode<3, 8, 6, YDT, FP8>), 48)
+    SQ_DECODE((k_gemm_decode<3, 8, 6, YDT, FP8>), narrow)
   }
   if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT, FP8>), 144)
-  SQ_DECODE((k_gemm_decode<3, 4, 5, YDT, FP8>), 48)
+  SQ_DECODE((k_gemm_decode<3, 4, 5, YDT, FP8>), narrow)
 #undef SQ_DECODE
+#undef SQ_GEMV
 }
 
 // Grid of a tiled GEMM kernel over ntiles tiles. Up to kPersistWaves tiles per
