@@ -215,8 +215,10 @@ GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 
                (3, 130, 320), (4, 16400, 1216), (2, 77, 704), (1, 1000, 4160),
                (1, 16400, 4160), (2, 16390, 704), (3, 20000, 320), (4, 16384, 64),
                # 1-2 tokens: the row GEMV up to K = 9216 (ragged N, K not a multiple of 1024), past it the
-               # GEMV (N >= 16384) or the MFMA decode kernel
-               (1, 9217, 9216), (2, 4099, 4160), (1, 5, 64), (2, 300, 9152),
+               # GEMV (N >= 16384) or the MFMA decode kernel; row counts that leave a last, partial round
+               # of rows over the 2048 waves (9216, 4099, 5000, 2100, 3072)
+               (1, 9217, 9216), (2, 4099, 4160), (1, 5, 64), (2, 300, 9152), (1, 9216, 9216), (1, 5000, 1088),
+               (2, 2100, 9216), (1, 3072, 4096),
                (1, 16400, 20480), (2, 3000, 13312)]
 
 
