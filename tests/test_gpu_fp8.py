@@ -188,7 +188,7 @@ def test_fp8_mfma_group_truncation():
 
 GEMM_SHAPES = [(17, 33, 128), (256, 256, 128), (300, 520, 384), (513, 700, 1280), (64, 16416, 2176),
                (1024, 2048, 20480), (5, 9, 133120),
-               # decode (M <= 128): every token-tile count, narrow and 144-channel strips, ragged N
+               # decode (M <= 128): every token-tile count, 3-tile and 9-tile strips, ragged N
                (1, 9216, 9216), (2, 1000, 1280), (4, 36864, 9216), (16, 130, 384), (33, 4000, 2048),
                (48, 16400, 1024), (64, 36864, 9216), (65, 300, 256), (128, 36864, 2048), (129, 300, 256),
                # N not a multiple of 4: the epilogue's partial stores, prefill and decode
@@ -214,7 +214,7 @@ def test_fp8_gemm_accumulator(shape):
 
 # Every token count the FP8 decode kernel serves up to 64 and a spread of 65-128 (eight token tiles),
 # and so every wave grid it picks, on narrow strips (4 channels at N = 300; 40 at N = 9250, the last
-# strip 10 rows) and on the 144-channel strips, three 128-byte segments.
+# strip 10 rows) and on 9-tile strips (68 channels at N = 16400), three 128-byte segments.
 @pytest.mark.parametrize("m", list(range(1, 65)) + [65, 80, 96, 127, 128])
 @pytest.mark.parametrize("n", [300, 9250, 16400])
 def test_fp8_gemm_decode_every_token_count(m, n):

@@ -206,8 +206,11 @@ GEMM_SHAPES = [(1, 1, 64), (1, 16, 64), (8, 100, 192), (17, 33, 128), (64, 520, 
                # decode kernel: every token-tile count, K tails of 64 / 128 / 192 bytes past a 256-byte segment
                (16, 48, 320), (32, 100, 576), (33, 17, 192), (48, 70, 4160), (63, 130, 2112), (64, 2048, 9216),
                (5, 36, 1984),
-               # decode kernel, 144-channel strips (N >= 16384): ragged last strip, K tails
+               # decode kernel, 9-tile strips (N >= 16384) of N / CUs channels rounded up to a multiple of 4
+               # (68 at N = 16400 and 16416, 64 at 16384, 116 at 28700, 80 at 20000): ragged last strips,
+               # K tails
                (33, 16400, 320), (20, 16384, 1088), (64, 16416, 2112), (12, 16400, 704), (9, 300, 1216),
+               (40, 28700, 320), (7, 20000, 192),
                # eight token tiles (65-128 tokens) on both strip widths, K tails; 129 takes the prefill tile
                (100, 9216, 9216), (128, 36864, 2112), (77, 16400, 1216), (129, 520, 640),
                # up to 4 tokens: the MFMA decode kernel below N = 16384, the GEMV from there; K tails inside a
@@ -237,13 +240,14 @@ def test_gemm_i32_exact(mnk):
 
 # The decode kernel picks its wave grid (token groups x channel groups) from the token-tile count and
 # the strip width: every token count up to 64 and a spread of 65-128 (eight token tiles), on a ragged
-# narrow strip (the MFMA kernel throughout) and on the 144-channel strips (the GEMV up to 4 tokens),
+# narrow strip (the MFMA kernel throughout) and on the 9-tile strips (the GEMV up to 4 tokens),
 # with an odd number of 64-byte K steps (the last segment's second half is the next row's bytes).
 DECODE_MS = list(range(1, 65)) + [65, 72, 80, 96, 111, 112, 127, 128]
 
 
-# Below N = 16384 a decode workgroup takes N / CUs channels rounded up to a multiple of 4 (4 at
-# N = 300, 40 at N = 9250 with a 10-row last strip), the 144-channel strips above.
+# A decode workgroup takes N / CUs channels rounded up to a multiple of 4, in 3 tiles below N = 16384
+# (4 at N = 300, 40 at N = 9250 with a 10-row last strip) and 9 tiles from there (68 at N = 16400,
+# a 12-row last strip).
 @pytest.mark.parametrize("m", DECODE_MS)
 @pytest.mark.parametrize("nk", [(300, 192), (9250, 256), (16400, 320)], ids=lambda s: "x".join(map(str, s)))
 def test_gemm_decode_every_token_count(m, nk):

@@ -1396,16 +1396,18 @@ hipError_t launch_rows(const GemmArgs& g, hipStream_t st) {
 // tokens at N >= 16384: the vector-ALU GEMV, 16 channels per workgroup (6.8
 // TB/s at N = 36864, where the MFMA kernel reaches 6.5). Otherwise the MFMA
 // decode kernel (gfx950 has no FP8 dot product on the vector ALUs, so FP8
-// always takes it) with up to 9 channel tiles per workgroup, so that each
-// token segment serves many weight tiles: 144-channel strips at N >= 16384
-// (256 workgroups at N = 36864). Below that, 3 tiles, but each workgroup
-// takes only its share of the channels, N / CUs rounded up to a multiple of 4
-// (36 at N = 9216: the third tile has 4 real rows, its other rows read zeros
-// without touching memory), so that every CU streams weights. Against 48
-// channels (192 workgroups at N = 9216) that took 4-64 tokens from 17.0-28.9
-// to 16.8-27.8 us (32 tokens: 21.7 to 19.4), and 8 tokens at N = 4096 from 8.8
-// to 8.5 us. 48-channel strips had beaten 64-channel ones (144 workgroups) by
-// 10-11% at 8-32 tokens. Measured on K = 9216, N = 9216 / 36864.
+// always takes it) with up to 9 channel tiles per workgroup at N >= 16384,
+// so that each token segment serves many weight tiles, and 3 below. Each
+// workgroup takes its share of the channels, N / CUs rounded up to a multiple
+// of 4, within 48 (3 tiles) or 48-144 (9 tiles), so that every CU streams
+// weights: 36 channels at N = 9216 (the third tile has 4 real rows; rows past
+// the strip read zeros without touching memory), 144 at N = 36864. Against
+// fixed 48- and 144-channel strips (192 workgroups at N = 9216, 114 at 16384,
+// 143 at 20480) that took 4-64 tokens at N = 9216 from 17.0-28.9 to 16.8-27.8
+// us (32 tokens: 21.7 to 19.4), N = 16384 from 32.8 / 41.6 / 49.6 to 30.4 /
+// 35.6 / 45.4 us at 8 / 32 / 64 tokens (K = 8192) and 16 tokens at N = 20480
+// from 41.6 to 34.3 us; 48-channel strips had beaten 64-channel ones (144
+// workgroups) by 10-11% at 8-32 tokens. Measured on K = 9216 unless stated.
 template <int YDT, bool FP8>
 hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
   const int mt = (g.M + 15) / 16;
@@ -1413,7 +1415,9 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
   int dev = 0, cus = 0;
   if (hipError_t e = hipGetDevice(&dev)) return e;
   if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return e;
-  const int narrow = min(48, max(4, ((g.N + max(cus, 1) - 1) / max(cus, 1) + 3) & ~3));   // channels per workgroup
+  const int per_cu = ((g.N + max(cus, 1) - 1) / max(cus, 1) + 3) & ~3;   // channels per workgroup:
+  const int narrow = min(48, max(4, per_cu));                              //   3-tile strips
+  const int wch = min(144, max(48, per_cu));                               //   9-tile strips
 #define SQ_DECODE(KERN, CH)                                                                                  \
   {                                                                                                          \
     hipLaunchKernelGGL(KERN, dim3((g.N + (CH) - 1) / (CH)), dim3(64 * kDecWaves), 0, st, g.xq, g.x_scale,   \
@@ -1436,22 +1440,22 @@ hipError_t launch_decode(const GemmArgs& g, hipStream_t st) {
     if (g.M <= 4) SQ_GEMV((k_gemv<4, 2, YDT>))
   }
   if (mt == 1) {
-    if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT, FP8>), 144)
+    if (wide) SQ_DECODE((k_gemm_decode<9, 1, 7, YDT, FP8>), wch)
     SQ_DECODE((k_gemm_decode<3, 1, 7, YDT, FP8>), narrow)
   }
   if (mt == 2) {
-    if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT, FP8>), 144)
+    if (wide) SQ_DECODE((k_gemm_decode<9, 2, 6, YDT, FP8>), wch)
     SQ_DECODE((k_gemm_decode<3, 2, 6, YDT, FP8>), narrow)
   }
   if (mt == 3) {
-    if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT, FP8>), 144)
+    if (wide) SQ_DECODE((k_gemm_decode<9, 3, 5, YDT, FP8>), wch)
     SQ_DECODE((k_gemm_decode<3, 3, 5, YDT, FP8>), narrow)
   }
   if (mt > 4) {                    // 65-128 tokens: eight token tiles, one ring stage fewer to fit LDS
-    if (wide) SQ_DECODE((k_gemm_decode<9, 8, 4, YDT, FP8>), 144)
+    if (wide) SQ_DECODE((k_gemm_decode<9, 8, 4, YDT, FP8>), wch)
     SQ_DECODE((k_gemm_decode<3, 8, 6, YDT, FP8>), narrow)
   }
-  if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT, FP8>), 144)
+  if (wide) SQ_DECODE((k_gemm_decode<9, 4, 5, YDT, FP8>), wch)
   SQ_DECODE((k_gemm_decode<3, 4, 5, YDT, FP8>), narrow)
 #undef SQ_DECODE
 #undef SQ_GEMV
