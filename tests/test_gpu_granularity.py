@@ -115,7 +115,7 @@ def test_norm_quant_static_far_below_range(dtype, factor):
 
 
 def test_norm_quant_static_product_overflow():
-    """binary32 values near 1e30 with a static step of 1e-12: y * fl32(1/step) overflows binary32,
+    """binary32 values near 1e30 with a static step of 1e-12: y times the reciprocal of the step overflows binary32,
     which must send those elements to the divide path (codes +-127, sign kept)."""
     g = torch.Generator().manual_seed(7)
     x = (torch.randn(5, 1024, generator=g) * 1e30).float()

@@ -353,10 +353,12 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
     const float step = FP8 ? fp8_step(amax) : int8_step(amax);
     if (threadIdx.x == 0) x_scale[row] = step;
     const typename std::conditional<FP8, QuantizerFp8, Quantizer>::type qz(step);
+    // every vector stores (a padding vector's offset lies past the codes' K
+    // bytes, so the store is dropped): no per-vector branch
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * THREADS;
-      if (vi < nvec) store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.codes8(v[i]));
+      store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.codes8(v[i]));
     }
   }
 }

@@ -279,30 +279,31 @@ __device__ __forceinline__ float int8_step(float amax) {
 // Per-row quantiser: code = clip(rne(fl32(y / step)), -127, 127).
 //
 // The quotient fl32(y / step) is needed only to decide which side of a
-// half-integer it falls on. The exact product P = y * fl32(1 / step) differs
-// from the exact quotient Q by at most |Q| 2^-24, and fl32(Q) from Q by at
-// most |Q| 2^-24, so for |Q| <= 128 fl32(Q) lies within 2^-16 of P: rne(P)
-// = rne(fl32(Q)) whenever P lies farther than 2^-16 from every half-integer.
+// half-integer it falls on. With r = v_rcp_f32(step), within one ulp (2^-23
+// relative) of 1 / step for steps in [2^-100, 2^126] (inputs and results
+// normal), the exact product P = y * r differs from the exact quotient Q by at
+// most |Q| 2^-23, and fl32(Q) from Q by at most |Q| 2^-24, so for |Q| <= 128
+// fl32(Q) lies within 1.5 * 2^-16 of P: rne(P) = rne(fl32(Q)) whenever P lies
+// farther than that from every half-integer.
 // One FMA gives s = fl(P + 1.5 * 2^23), which is 1.5 * 2^23 + rne(P) for
 // |P| < 2^22 (the binary32 spacing there is 1, ties to even, and 1.5 * 2^23
 // is even), so the low byte of s's bits is rne(P) in two's complement; a
 // second FMA gives the residual d = fl(P - rne(P)) (one rounding of a value
 // below 1/2, within 2^-25). Elements with |d| >= 1/2 - 2^-15 (P within about
-// 2^-15 of a half-integer) take the IEEE division. Steps below 2^-100 (where
-// 1/step may overflow) always divide. (Only a step given for a whole tensor
-// can exceed 2^126, where fl32(1 / step) is subnormal and coarser; then
-// |Q| <= FLT_MAX / step < 4 and |P - Q| < 2^-21, still inside the margin.)
+// 2^-15 of a half-integer) take the IEEE division, and so do all elements for
+// steps outside [2^-100, 2^126] (where 1/step would leave the normal range;
+// only a step given for a whole tensor can exceed 2^126).
 struct Quantizer {
   static constexpr float kMagic = 12582912.0f;         // 1.5 * 2^23
   float step, rcp;
   bool zero, exact_only;
   __device__ __forceinline__ explicit Quantizer(float st) : step(st) {
     zero = !(st > 0.0f);
-    exact_only = st < 0x1p-100f;
-    rcp = zero ? 0.0f : div_rn(1.0f, st);
+    exact_only = !(st >= 0x1p-100f && st <= 0x1p126f);
+    rcp = __builtin_amdgcn_rcpf(st);                     // v_rcp_f32: within one ulp of 1 / st
   }
   // Codes of 8 values, packed little-endian into two 32-bit words. With the
-  // row's own step |P| <= amax * fl32(1/step) < 127.5, so rne(P) needs no
+  // row's own step |P| <= amax * r < 127.5, so rne(P) needs no
   // clamp; CLIP (a step given for a whole tensor, which values may exceed)
   // clamps s to 1.5 * 2^23 +- 127. For |P| >= 2^22 s is no longer
   // 1.5 * 2^23 + rne(P), but it stays on P's side of that range, so the clamp
@@ -344,8 +345,8 @@ struct Quantizer {
 __device__ __forceinline__ float fp8_step(float amax) { return div_rn(amax, 448.0f); }
 
 // Per-row FP8 quantiser: code = E4M3(fl32(y / step)), round half to even
-// (v_cvt_pk_fp8_f32 rounds that way; gfx950 converts to OCP E4M3). As in
-// Quantizer, t = fl32(y * fl32(1 / step)) stands in for the quotient q: with
+// (v_cvt_pk_fp8_f32 rounds that way; gfx950 converts to OCP E4M3). Here
+// t = fl32(y * fl32(1 / step)) stands in for the quotient q: with
 // |t| in [2^e, 2^(e+1)), |t - q| <= |q| 2^-23 (1 + 2^-25) is below 2.0001 ulps
 // of t, and below one ulp of t when q < 2^e, so q lies strictly between the
 // binary32 values 4 bit steps below and above t (the step below 2^e is half
