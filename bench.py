@@ -78,6 +78,9 @@ def parse():
     p.add_argument("--summarize-ln-counters", metavar="PMC_DIR",
                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU GRBM_GUI_ACTIVE run of this benchmark into a "
                         "profiles/ table of the LayerNorm quantiser's vector-ALU issue and exit")
+    p.add_argument("--summarize-ln-waits", metavar="PMC_DIR",
+                   help="turn a rocprofv3 --pmc run of the LayerNorm wave-state counters into a profiles/ table "
+                        "and exit")
     p.add_argument("--summarize-prefill", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace of --prefill-sweep into a profiles/ table and exit")
     return p.parse_args()
@@ -526,6 +529,51 @@ def summarize_ln_counters(pmc_dir, m=8192, k=20480):
                      f"{cyc / d['ns']:.2f} | {64.0 * d['SQ_INSTS_VALU'] / (m * k):.1f} | "
                      f"{d['SQ_INSTS_VALU'] / (N_CU * cyc):.2f} |")
     with open(os.path.join(ROOT, "profiles", "norm_quant_layernorm_valu_mtnlg530b.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+LN_WAIT_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_BUSY_CYCLES "
+                    "SQ_INSTS_VALU SQ_WAVES GRBM_GUI_ACTIVE")
+
+
+def summarize_ln_waits(pmc_dir):
+    """Where the LayerNorm quantiser's waves spend their time (MT-NLG width, 8192 x 20480 fp16). The SQ
+    wave-state counters count quad-cycles summed over every wave: working on an instruction
+    (SQ_ACTIVE_INST_ANY), ready but not yet issued because other waves hold the unit
+    (SQ_WAIT_INST_ANY), and waiting on a counter or barrier (SQ_WAIT_ANY), each over the waves' lifetime
+    (SQ_WAVE_CYCLES). One wave64 VALU instruction holds its SIMD for one quad-cycle, so the SIMDs'
+    VALU share is SQ_ACTIVE_INST_VALU over (SIMDs x quad-cycles of the dispatch)."""
+    import glob
+    from collections import defaultdict
+    hits = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no counter collection under {pmc_dir}")
+    per = defaultdict(lambda: defaultdict(float))
+    for r in _read_csv(hits[0]):
+        if "sq::k_norm_quant<sq::f16_t, 1," in r["Kernel_Name"]:
+            d = per[int(r["Dispatch_Id"])]
+            d[r["Counter_Name"]] += float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        raise SystemExit("no LayerNorm quantiser dispatch in the run")
+    cmd = (f"rocprofv3 --pmc {LN_WAIT_COUNTERS} -d <dir> -o run --output-format csv -- "
+           "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-decode --no-clock")
+    lines = ["# LayerNorm quantiser wave states (rocprofv3 --pmc): MT-NLG width, 8192 x 20480 fp16", "",
+             f"Command: `{cmd}`, then `python bench.py --summarize-ln-waits <dir>`.", "",
+             "Kernel `sq::k_norm_quant<sq::f16_t, 1, 5, 512, 0>`: 512 threads (8 waves) per workgroup, two "
+             "workgroups per CU (122 VGPRs: four waves per SIMD). Shares of the waves' lifetime "
+             "(SQ_WAVE_CYCLES); SIMD VALU busy = SQ_ACTIVE_INST_VALU / (1024 SIMDs x dispatch cycles / 4).", "",
+             "| dispatch | ms | waves | instruction in progress | ready, waiting for issue | waiting on a counter "
+             "or barrier | SIMD VALU busy |",
+             "|---|---|---|---|---|---|---|"]
+    for i, (_, d) in enumerate(sorted(per.items())):
+        wc = d["SQ_WAVE_CYCLES"]
+        quads = d["GRBM_GUI_ACTIVE"] / N_XCD / 4
+        lines.append(f"| {'warm-up' if i == 0 and len(per) > 1 else 'timed'} | {d['ns'] / 1e6:.4f} | "
+                     f"{int(d['SQ_WAVES'])} | {d['SQ_ACTIVE_INST_ANY'] / wc:.2f} | {d['SQ_WAIT_INST_ANY'] / wc:.2f} | "
+                     f"{d['SQ_WAIT_ANY'] / wc:.2f} | {d['SQ_ACTIVE_INST_VALU'] / (4 * N_CU * quads):.2f} |")
+    with open(os.path.join(ROOT, "profiles", "norm_quant_layernorm_waits_mtnlg530b.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -1228,6 +1276,9 @@ def main():
         return
     if args.summarize_ln_counters:
         summarize_ln_counters(args.summarize_ln_counters)
+        return
+    if args.summarize_ln_waits:
+        summarize_ln_waits(args.summarize_ln_waits)
         return
     if args.summarize_prefill:
         summarize_prefill(args.summarize_prefill)
