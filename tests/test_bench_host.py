@@ -1,5 +1,5 @@
 """Host logic of bench.py on the CPU: the refusal of runs on several GPUs, the counter summaries it
-derives from rocprofv3 CSVs (shader clock and MFMA busy, per-dispatch kernel tables), the traffic
+derives from rocprofv3 CSVs (shader clock and MFMA busy, wave states, per-dispatch kernel tables), the traffic
 record's staleness check, and the algorithmic byte counts. Synthetic CSVs stand in for rocprofv3
 output; nothing here touches a GPU or the committed profiles."""
 import csv
@@ -148,3 +148,21 @@ def test_clock_sampler_reads_board_power_and_cap(tmp_path):
     (hw / "power1_average").write_text("900000000\n")
     assert bench.ClockSampler(str(f)).read_watts() == 900.0
     assert bench.ClockSampler(str(tmp_path / "pp_dpm_sclk"), hwmon=str(tmp_path / "none")).power_path is None
+
+
+def test_ln_wave_states_from_counters(scratch_root):
+    # one dispatch of 4096 waves over 200,000 cycles per XCD (0.1 ms): each wave lives 200 quad-cycles
+    # of which 50 on an instruction, 40 ready but not issued and 110 waiting; the SIMDs' VALU holds
+    # 0.6 of the dispatch's quad-cycles
+    header = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    quads = 200_000 / 4
+    vals = {"SQ_WAVE_CYCLES": 4096 * 200, "SQ_ACTIVE_INST_ANY": 4096 * 50, "SQ_WAIT_INST_ANY": 4096 * 40,
+            "SQ_WAIT_ANY": 4096 * 110, "SQ_ACTIVE_INST_VALU": 0.6 * 1024 * quads, "SQ_WAVES": 4096,
+            "GRBM_GUI_ACTIVE": 8 * 200_000, "SQ_INSTS_VALU": 1.0, "SQ_BUSY_CYCLES": 1.0}
+    rows = [[9, "void sq::k_norm_quant<sq::f16_t, 1, 5, 512, 0>(...)", k, v, 0, 100_000] for k, v in vals.items()]
+    rows.append([3, "void sq::k_gemm_tile<1, 4>(...)", "SQ_WAVES", 1, 0, 10])
+    _write_csv(scratch_root / "w" / "run_counter_collection.csv", header, rows)
+    bench.summarize_ln_waits(str(scratch_root / "w"))
+    text = (scratch_root / "profiles" / "norm_quant_layernorm_waits_mtnlg530b.md").read_text()
+    body = [ln for ln in text.splitlines() if ln.startswith("| timed")]
+    assert body == ["| timed | 0.1000 | 4096 | 0.25 | 0.20 | 0.55 | 0.60 |"]
