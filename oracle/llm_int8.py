@@ -41,10 +41,10 @@ from __future__ import annotations
 import numpy as np
 
 from .smoothquant_oracle import (LAYERNORM, NONE, RMSNORM, dequantize, f32_to_bf16_bits, int_gemm, normalize,
-                                 quantize_rows, round_output, row_stats, widen)
+                                 quantize_rows, row_stats, widen)
 
 __all__ = ["TAU", "outlier_channels", "half_format", "round16", "weights", "activations", "gemm16",
-           "gemm16_bound", "decompose", "output_bound", "reference_output"]
+           "gemm16_bound", "decompose", "output_bound"]
 
 F32 = np.float32
 F64 = np.float64
@@ -169,8 +169,3 @@ def output_bound(d, n_pad=None):
         e = np.floor(np.log2(np.maximum(mag, tiny)))
     half_ulp = np.maximum(2.0 ** (e - p), tiny / 2)
     return e32 + half_ulp
-
-
-def reference_output(d):
-    """The oracle's own binary32 evaluation, converted to the output type (for display; checks use ref)."""
-    return round_output(d["ref"].astype(F32), d["out_dtype"])
