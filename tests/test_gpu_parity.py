@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import w8a8_int8_linear_amd as sq
 from synth import rand_int8, rand_positive, rand_tokens, to_numpy
-from tests.gpu_check import bits, check_calibrate, check_fold, check_norm_quant, check_output, host
+from tests.gpu_check import check_calibrate, check_fold, check_norm_quant, check_output, host
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32

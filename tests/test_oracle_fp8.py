@@ -5,7 +5,6 @@ FP8 GEMM with its accumulation bound. CPU only."""
 from fractions import Fraction
 
 import numpy as np
-import pytest
 import torch
 
 import oracle as O
