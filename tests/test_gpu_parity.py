@@ -359,9 +359,12 @@ def test_gemm_minus_128_codes_up_to_their_k_limit():
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("bias", [False, True])
 # 16-bit outputs of the tiled kernels go out 8 columns per lane when N % 8 == 0 (ragged last tile
-# included), element by element otherwise; K % 128 == 64 takes the 64-byte kernel
+# included), element by element otherwise; K % 128 == 64 takes the 64-byte kernel. The decode paths
+# have epilogues of their own: the row GEMV (1 x 72), the wide GEMV (up to 4 tokens from N = 16384,
+# N % 4 both ways), 3-tile and 9-tile strips (40 tokens) and eight token tiles (100 tokens).
 @pytest.mark.parametrize("mnk", [(1, 72, 64), (40, 300, 512), (300, 520, 192), (777, 1030, 1024),
-                                 (777, 1032, 1024), (300, 776, 192), (257, 1028, 256)],
+                                 (777, 1032, 1024), (300, 776, 192), (257, 1028, 256),
+                                 (3, 16400, 128), (2, 16390, 64), (40, 16402, 192), (100, 522, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_gemm_dequant(out, bias, mnk):
     m, n, k = mnk
