@@ -264,7 +264,10 @@ def test_fp8_gemm_persistent_grid(shape):
 
 
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("mnk", [(300, 520, 1280), (257, 1030, 384)], ids=lambda s: "x".join(map(str, s)))
+# prefill tiles, then the decode kernel's FP8 mode: one token, 3-tile strips, 9-tile strips (N % 4 != 0)
+# and eight token tiles
+@pytest.mark.parametrize("mnk", [(300, 520, 1280), (257, 1030, 384), (1, 72, 128), (40, 1000, 256),
+                                 (8, 16402, 128), (100, 522, 256)], ids=lambda s: "x".join(map(str, s)))
 def test_fp8_gemm_dequantised_output(out, mnk):
     m, n, k = mnk
     xq = _codes((m, k), 5, 30.0)
