@@ -274,12 +274,20 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
     // (8 NV VGPRs, within the 128 of two workgroups per CU) and refill the raw
     // buffer before the reduction; wider ones recompute x * gamma in pass two.
     constexpr bool kKeepY = THREADS <= 512 && Storage<T>::kBytes == 2 && NV <= 5;
+    // Wide rows with every column factor on chip (padding vectors hold zero
+    // factors, and their raw vectors read zeros) run both passes with no
+    // per-vector branch: each padding store falls past the codes' K bytes and
+    // is dropped. The wait-counter pass then tracks each vector's refill
+    // separately, and pass one starts on vector 0 of the next row while later
+    // vectors are still in flight. Behind per-vector branches it waited for
+    // the whole row first (vmcnt(0)).
+    constexpr bool kFlat = !kKeepY && GREG + GLDS == NV;
     float ys[kKeepY ? NV : 1][8];
     float pm[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       pm[i] = 0.0f;
-      if (static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
+      if (kFlat || static_cast<int>(threadIdx.x) + i * THREADS < nvec) {
         float y[8];
         none_y(raw, i, gv, y);
 #pragma unroll
@@ -287,6 +295,12 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
           pm[i] = fmaxf(pm[i], fabsf(y[e]));
           if constexpr (kKeepY) ys[i][e] = y[e];
         }
+      }
+      if constexpr (kFlat) {
+        // one vector at a time, as the branches kept it: each vector's max is
+        // formed here rather than in one tree over every vector's products
+        asm volatile("" : "+v"(pm[i]));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if constexpr (kKeepY) {
@@ -316,15 +330,21 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
 #pragma unroll
       for (int i = 0; i < NV; ++i) opaque(raw.r[i].a);
       memory_opaque();
+      // (kFlat) the vector index base, opaque per row: hoisted out of the row
+      // loop, the 2 NV code and refill offsets would each hold a register
+      uint32_t ob = threadIdx.x;
+      if constexpr (kFlat) asm volatile("" : "+v"(ob));
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int vi = threadIdx.x + i * THREADS;
-        if (vi < nvec) {
+        if (kFlat || vi < nvec) {
           float y[8];
           none_y(raw, i, gv, y);
-          store_codes8_buf(rq, static_cast<uint32_t>(vi) * 8, qz.codes8(y));
-          if (refill) raw_load_buf<T>(rn, RR::off(i), raw.r[i]);
+          const uint32_t v = kFlat ? ob + static_cast<uint32_t>(i * THREADS) : static_cast<uint32_t>(vi);
+          store_codes8_buf(rq, v * 8, qz.codes8(y));
+          if (refill) raw_load_buf<T>(rn, kFlat ? v * (8 * Storage<T>::kBytes) : RR::off(i), raw.r[i]);
         }
+        if constexpr (kFlat) __builtin_amdgcn_sched_barrier(0);
       }
     }
   } else {
