@@ -562,7 +562,7 @@ def summarize_ln_waits(pmc_dir):
     lines = ["# LayerNorm quantiser wave states (rocprofv3 --pmc): MT-NLG width, 8192 x 20480 fp16", "",
              f"Command: `{cmd}`, then `python bench.py --summarize-ln-waits <dir>`.", "",
              "Kernel `sq::k_norm_quant<sq::f16_t, 1, 5, 512, 0>`: 512 threads (8 waves) per workgroup, two "
-             "workgroups per CU (122 VGPRs: four waves per SIMD). Shares of the waves' lifetime "
+             "workgroups per CU (116 VGPRs and 64 KiB of LDS each: four waves per SIMD). Shares of the waves' lifetime "
              "(SQ_WAVE_CYCLES); SIMD VALU busy = SQ_ACTIVE_INST_VALU / (1024 SIMDs x dispatch cycles / 4).", "",
              "| dispatch | ms | waves | instruction in progress | ready, waiting for issue | waiting on a counter "
              "or barrier | SIMD VALU busy |",

@@ -46,6 +46,53 @@ struct RawRow {
 static __constant__ float kOnes8[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
 static __constant__ float kZeros8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 
+// On-chip copy of the norm's gamma (and LayerNorm's beta) for the first GB
+// vectors of each thread, kept for the workgroup's lifetime: every row reads
+// them, and from memory those loads wait, in issue order, behind the next
+// row's refill. Each thread reads back only what it wrote (no barrier). GB
+// fills a share of LDS that leaves room for the layout's workgroups per CU:
+// 32 / 64 / 128 KiB for 256 / 512 / 1024 threads; rows of fewer than 4
+// vectors per thread keep GB = 0.
+template <int NORM, int GB, int THREADS>
+struct NormCache {
+  static constexpr int kParts = NORM == SQ_NORM_LAYERNORM ? 2 : 1;   // gamma (and beta)
+  static constexpr int kFloat4 = GB > 0 ? GB * kParts * 2 * THREADS : 1;
+  static __device__ __forceinline__ void init(float4* c, const float* __restrict__ gamma,
+                                              const float* __restrict__ beta, int nvec) {
+#pragma unroll
+    for (int i = 0; i < GB; ++i) {
+      const int vi = threadIdx.x + i * THREADS;
+#pragma unroll
+      for (int part = 0; part < kParts; ++part) {
+        const float* src = part == 0 ? gamma : beta;
+        float w[8] = {part == 0 ? 1.0f : 0.0f, part == 0 ? 1.0f : 0.0f, part == 0 ? 1.0f : 0.0f,
+                      part == 0 ? 1.0f : 0.0f, part == 0 ? 1.0f : 0.0f, part == 0 ? 1.0f : 0.0f,
+                      part == 0 ? 1.0f : 0.0f, part == 0 ? 1.0f : 0.0f};
+        if (src != nullptr && vi < nvec) load8_f32(src + 8 * vi, w);
+        c[((i * kParts + part) * 2) * THREADS + threadIdx.x] = make_float4(w[0], w[1], w[2], w[3]);
+        c[((i * kParts + part) * 2 + 1) * THREADS + threadIdx.x] = make_float4(w[4], w[5], w[6], w[7]);
+      }
+    }
+  }
+  static __device__ __forceinline__ void get(const float4* __restrict__ c, int i, float g[8], float b[8]) {
+    const float4 g0 = c[((i * kParts) * 2) * THREADS + threadIdx.x];
+    const float4 g1 = c[((i * kParts) * 2 + 1) * THREADS + threadIdx.x];
+    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    if constexpr (kParts == 2) {
+      const float4 b0 = c[((i * kParts + 1) * 2) * THREADS + threadIdx.x];
+      const float4 b1 = c[((i * kParts + 1) * 2 + 1) * THREADS + threadIdx.x];
+      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+    }
+  }
+};
+template <int NORM, int NV, int THREADS>
+constexpr int norm_cache_vectors() {
+  if (NORM == SQ_NORM_NONE || NV < 4) return 0;
+  const int budget = THREADS >= 1024 ? 131072 : THREADS >= 512 ? 65536 : 32768;
+  const int per = (NORM == SQ_NORM_LAYERNORM ? 2 : 1) * 32 * THREADS;
+  return budget / per < NV ? budget / per : NV;
+}
+
 // Statistics of a binary32 row held in registers (padding holds zeros) and the
 // normalised y in place: LayerNorm ((x - mean) * rstd) * gamma + beta, RMSNorm
 // (x * rstd) * gamma; a NULL gamma / beta means 1 / 0. Sums are taken in
@@ -53,10 +100,13 @@ static __constant__ float kZeros8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f
 // variance in one pass where that is provably accurate enough, else centred on
 // the binary64 mean); rstd = fl32(1 / fl32(sqrt(fl32(var + eps)))). With st
 // non-NULL, thread 0 also writes (mean, rstd) there (mean 0 for RMSNorm).
-template <int NORM, int NV, int THREADS>
+// With GB > 0, gamma and beta of the thread's vectors [0, GB) are read from
+// gbl, the workgroup's on-chip copy (NormCache below), instead of memory.
+template <int NORM, int NV, int THREADS, int GB = 0>
 __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const float* __restrict__ gamma,
                                               const float* __restrict__ beta, float eps, RedRing<THREADS>& red,
-                                              int& rk, float* __restrict__ st = nullptr) {
+                                              int& rk, float* __restrict__ st = nullptr,
+                                              const float4* __restrict__ gbl = nullptr) {
   const int nvec = K >> 3;
   // 1/K in binary64, the same for every row: a product with it is within 2^-52
   // relative of the quotient, far inside the 2^-12-spacing near-tie margin of
@@ -153,8 +203,12 @@ __device__ __forceinline__ void normalize_row(float (&v)[NV][8], int K, const fl
     const int vi = threadIdx.x + i * THREADS;
     if (vi >= nvec) continue;
     float g[8], b[8];
-    load8_f32_buf(rg, (32u * static_cast<uint32_t>(vi)) & gmask, g);
-    if constexpr (NORM == SQ_NORM_LAYERNORM) load8_f32_buf(rb, (32u * static_cast<uint32_t>(vi)) & bmask, b);
+    if (i < GB) {
+      NormCache<NORM, GB, THREADS>::get(gbl, i < GB ? i : 0, g, b);
+    } else {
+      load8_f32_buf(rg, (32u * static_cast<uint32_t>(vi)) & gmask, g);
+      if constexpr (NORM == SQ_NORM_LAYERNORM) load8_f32_buf(rb, (32u * static_cast<uint32_t>(vi)) & bmask, b);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float t = v[i][e];
@@ -252,14 +306,16 @@ __device__ __forceinline__ void none_y(const RawRow<T, NV, THREADS>& raw, int i,
 //  LayerNorm / RMSNorm: widen once (the whole buffer is then refilled),
 //        normalise in place, then max and codes; STATS also writes the
 //        row's (mean, rstd) to stats[2 row], stats[2 row + 1].
-template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS, bool FP8 = false, bool STATS = false>
+template <typename T, int NORM, int NV, int THREADS, int GREG, int GLDS, bool FP8 = false, bool STATS = false,
+          int GB = 0>
 __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const void* __restrict__ x,
                                              int64_t row, int64_t next, int M, int K,
                                              const float* __restrict__ gamma,
                                              const ColVec<NV, THREADS, GREG, GLDS>& gv,
                                              const float* __restrict__ beta, float eps, int8_t* __restrict__ xq,
                                              float* __restrict__ x_scale, RedRing<THREADS>& red, int& rk,
-                                             float* __restrict__ stats = nullptr) {
+                                             float* __restrict__ stats = nullptr,
+                                             const float4* __restrict__ gbl = nullptr) {
   const int nvec = K >> 3;
   using RR = RawRow<T, NV, THREADS>;
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(xq + row * K, static_cast<uint32_t>(K));   // this row's codes
@@ -366,7 +422,7 @@ __device__ __forceinline__ void quantize_row(RawRow<T, NV, THREADS>& raw, const 
         }
       }
     }
-    normalize_row<NORM, NV, THREADS>(v, K, gamma, beta, eps, red, rk, STATS ? stats + 2 * row : nullptr);
+    normalize_row<NORM, NV, THREADS, GB>(v, K, gamma, beta, eps, red, rk, STATS ? stats + 2 * row : nullptr, gbl);
     float pm[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -522,11 +578,17 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
   constexpr int kReg = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kReg : 0;
   constexpr int kLds = NORM == SQ_NORM_NONE ? ColSplit<T, NV, THREADS>::kLds : 0;
   __shared__ float4 gl[kLds > 0 ? 2 * kLds * THREADS : 1];
+  // the norms' per-token passes keep gamma / beta of their first vectors on chip
+  constexpr bool kPerToken = !(MODE == kRowsAmax || MODE == kRowsGivenStep || MODE == kRowsFp8GivenStep);
+  constexpr int kGB = kPerToken ? norm_cache_vectors<NORM, NV, THREADS>() : 0;
+  using NC = NormCache<NORM, kGB, THREADS>;
+  __shared__ float4 gbl[NC::kFloat4];
   ColVec<NV, THREADS, kReg, kLds> gv;
   const int64_t G = gridDim.x;
   RawRow<T, NV, THREADS> raw;
   raw.load(x, blockIdx.x, K);
   gv.init(NORM == SQ_NORM_NONE ? gamma : nullptr, K >> 3, gl);
+  NC::init(gbl, gamma, beta, K >> 3);
   int rk = 0;
   if constexpr (MODE == kRowsAmax || MODE == kRowsGivenStep || MODE == kRowsFp8GivenStep) {
     // per-tensor passes (step_ptr and write_scale are used only here); the FP8
@@ -539,8 +601,8 @@ __global__ __launch_bounds__(THREADS) void k_norm_quant(const void* __restrict__
                                                        red, rk, qz, write_scale != 0);
   } else {
     for (int64_t row = blockIdx.x; row < M; row += G)
-      quantize_row<T, NORM, NV, THREADS, kReg, kLds, MODE == kRowsFp8, MODE == kRowsStats>(
-          raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk, stats);
+      quantize_row<T, NORM, NV, THREADS, kReg, kLds, MODE == kRowsFp8, MODE == kRowsStats, kGB>(
+          raw, x, row, row + G, M, K, gamma, gv, beta, eps, xq, x_scale, red, rk, stats, gbl);
   }
 }
 
