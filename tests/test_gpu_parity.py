@@ -123,6 +123,33 @@ def test_norm_quant_none_many_rows(dtype, k):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("k", [8192, 16384, 20480])
+def test_norm_quant_norms_many_rows(dtype, norm, k):
+    # more rows than resident workgroups: each workgroup reuses its on-chip
+    # gamma / beta of the first vectors (256 x 4, 512 x 4 and 512 x 5 layouts)
+    # over several rows while the next row streams in; every row checked
+    m = 600
+    seed = _seed("nqn", dtype, norm, m, k)
+    x = rand_tokens(m, k, dtype, seed, n_outliers=k // 2000, outlier_scale=60.0)
+    gamma, beta = params(k, seed + 1, norm)
+    xq, xs = sq.sq_norm_quant(cuda(x), norm, cuda(gamma), cuda(beta), 1e-5)
+    torch.cuda.synchronize()
+    check_norm_quant(to_numpy(x), dtype, norm, np_or_none(gamma), np_or_none(beta), 1e-5, host(xq), host(xs),
+                     label=f"{dtype}/{norm}/{m}x{k}")
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_norm_quant_norms_many_rows_without_params(norm):
+    # no gamma / beta: the on-chip copy holds the stand-ins 1 and 0
+    m, k = 600, 20480
+    x = rand_tokens(m, k, "f16", _seed("nqn0", norm), n_outliers=10, outlier_scale=60.0)
+    xq, xs = sq.sq_norm_quant(cuda(x), norm, None, None, 1e-5)
+    torch.cuda.synchronize()
+    check_norm_quant(to_numpy(x), "f16", norm, None, None, 1e-5, host(xq), host(xs), label=f"noparams/{norm}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_layernorm_mean_offsets(dtype):
     # LayerNorm statistics on both sides of the kernel's switch between the
     # one-pass variance (sum x^2 <= 256 sum (x - mean)^2) and the centred
